@@ -1,0 +1,36 @@
+/*
+ * Oracle ABI (TEST INFRASTRUCTURE ONLY). Host pointers, C-contiguous:
+ *   u, delta, z, out : [batch, dim, seqlen]
+ *   B, C             : [batch, dstate, seqlen]
+ *   A                : [dim, dstate]
+ *   D, delta_bias    : [dim]
+ *   h0, final_state  : [batch, dim, dstate]
+ * D, z, delta_bias, h0 and final_state may be NULL (no skip, no gate, zero bias, zero
+ * initial state, state not returned). nthreads <= 0 means one thread.
+ * Returns 0, -1 for a bad argument, -2 if a row's scratch could not be allocated.
+ */
+#ifndef SSM_REF_H
+#define SSM_REF_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int ssm_ref_scan_f64(const double* u, const double* delta, const double* A, const double* B,
+                     const double* C, const double* D, const double* z,
+                     const double* delta_bias, int delta_softplus, const double* h0,
+                     double* out, double* final_state, int64_t batch, int64_t dim,
+                     int64_t dstate, int64_t seqlen, int nthreads);
+
+int ssm_ref_scan_f32(const float* u, const float* delta, const float* A, const float* B,
+                     const float* C, const float* D, const float* z,
+                     const float* delta_bias, int delta_softplus, const float* h0,
+                     float* out, float* final_state, int64_t batch, int64_t dim,
+                     int64_t dstate, int64_t seqlen, int nthreads);
+
+int ssm_ref_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,163 @@
+"""Seeded input generation for the selective-scan forward.
+
+The value distributions follow the pages' description of a Mamba-1 layer scan:
+  * input u and a raw step size drawn per (batch, channel, time);
+  * a per-channel step-size bias chosen so that softplus(bias) is uniform in
+    [1e-3, 1e-1] (the usual Mamba dt initialisation; softplus(log(expm1(dt))) = dt);
+  * diagonal A with the S4D-real pattern A[d, n] = -(n + 1), or that pattern scaled per
+    (channel, state) by U(0.5, 1.5) for the wide-state workload;
+  * input-dependent B and C of shape [batch, dstate, seqlen], shared by all channels;
+  * a skip weight D per channel and, for gated workloads, a gate input z.
+
+Draw order (one numpy PCG64 stream per workload, seeded with the workload's seed), each
+array drawn in C order of its shape:
+  1. u      ~ N(0, 1)             [batch, dim, seqlen]
+  2. delta  ~ 0.5 * N(0, 1)       [batch, dim, seqlen]   (raw, before bias and softplus)
+  3. dt     ~ U(1e-3, 1e-1)       [dim]  ->  delta_bias = log(expm1(dt))
+  4. B      ~ bc_scale * N(0, 1)  [batch, dstate, seqlen]
+  5. C      ~ bc_scale * N(0, 1)  [batch, dstate, seqlen]
+  6. D      ~ N(0, 1)             [dim]
+  7. z      ~ N(0, 1)             [batch, dim, seqlen]   (gated workloads only)
+  8. s      ~ U(0.5, 1.5)         [dim, dstate]          (scaled-A workloads only)
+  9. h0     ~ N(0, 1)             [batch, dim, dstate]   (workloads that start from a state)
+
+Normal draws are made in float32. For bf16 workloads, u, delta, B, C and z are rounded
+once from float32 to bfloat16 with round-to-nearest-even; the stored bits are what both
+the GPU path and the oracle read. A, D, delta_bias and h0 are always float32.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    seqlen: int
+    io: str = "f32"            # storage dtype of u, delta, B, C, z, out: "f32" or "bf16"
+    gate: bool = False         # z present (out = y * silu(z))
+    a_kind: str = "s4d"        # "s4d": A = -(n+1);  "scaled": A = -(n+1) * U(0.5, 1.5)
+    bc_scale: float = 1.0      # standard deviation of B and C
+    initial_state: bool = False
+    seed: int = 0
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.seqlen
+
+    @property
+    def tuples(self) -> int:
+        return self.batch * self.dim * self.seqlen * self.dstate
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the operation must move: each input read once, each output written once."""
+        s = 2 if self.io == "bf16" else 4
+        per_elem = s * (2 + (1 if self.gate else 0) + 1)            # u, delta, [z], out
+        n = self.batch * self.dim * self.seqlen * per_elem
+        n += self.batch * self.dstate * self.seqlen * 2 * s          # B, C
+        n += self.dim * self.dstate * 4 + self.dim * 4 * 2           # A, D, delta_bias
+        n += self.batch * self.dim * self.dstate * 4                 # final_state written
+        if self.initial_state:
+            n += self.batch * self.dim * self.dstate * 4             # h0 read
+        return n
+
+    def describe(self) -> str:
+        gate = " gated" if self.gate else ""
+        h0 = " from-h0" if self.initial_state else ""
+        return (f"{self.name}: b{self.batch} d{self.dim} N{self.dstate} L{self.seqlen} "
+                f"{self.io}{gate}{h0}")
+
+
+# The workloads the pages' problem statement is measured on.  "layer" is the headline:
+# a Mamba-1 layer's scan at batch 4, 2048 channels, 16 states, 2048 steps, bf16 I/O.
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", 1, 64, 16, 256, "f32", seed=0),
+    "long": Workload("long", 2, 512, 16, 8192, "f32", seed=1),
+    "layer": Workload("layer", 4, 2048, 16, 2048, "bf16", gate=True, seed=2),
+    "verylong": Workload("verylong", 1, 1536, 16, 65536, "f32", seed=3),
+    "widestate": Workload("widestate", 8, 2048, 64, 4096, "bf16", gate=True,
+                          a_kind="scaled", bc_scale=0.125, seed=4),
+    "decode": Workload("decode", 8, 2048, 64, 1, "bf16", gate=True, a_kind="scaled",
+                       bc_scale=0.125, initial_state=True, seed=4),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16, nearest-even; returns the uint16 bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))
+               >> np.uint32(16)).astype(np.uint16)
+    nan = (b & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if nan.any():
+        rounded[nan] = np.uint16(0x7FC0)
+    return rounded
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def widen(x: Optional[np.ndarray], io: str) -> Optional[np.ndarray]:
+    """Stored values (float32 array or bf16 bits) as float64, exactly."""
+    if x is None:
+        return None
+    if io == "bf16" and x.dtype == np.uint16:
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def _store(x: np.ndarray, io: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if io == "bf16" else np.ascontiguousarray(x, np.float32)
+
+
+def make_inputs(w: Workload) -> Dict[str, Optional[np.ndarray]]:
+    """Draw one workload's inputs. Streamed arrays come back in storage form."""
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    Bn, Dd, N, L = w.batch, w.dim, w.dstate, w.seqlen
+    f32 = np.float32
+
+    u = rng.standard_normal((Bn, Dd, L), dtype=f32)
+    delta = rng.standard_normal((Bn, Dd, L), dtype=f32) * f32(0.5)
+    dt = rng.uniform(1e-3, 1e-1, size=Dd)
+    delta_bias = np.log(np.expm1(dt)).astype(f32)
+    Bm = rng.standard_normal((Bn, N, L), dtype=f32)
+    Cm = rng.standard_normal((Bn, N, L), dtype=f32)
+    if w.bc_scale != 1.0:
+        Bm *= f32(w.bc_scale)
+        Cm *= f32(w.bc_scale)
+    Dv = rng.standard_normal(Dd, dtype=f32)
+    z = rng.standard_normal((Bn, Dd, L), dtype=f32) if w.gate else None
+    idx = np.arange(1, N + 1, dtype=np.float64)
+    if w.a_kind == "s4d":
+        A = np.broadcast_to(-idx, (Dd, N)).astype(f32)
+    elif w.a_kind == "scaled":
+        s = rng.uniform(0.5, 1.5, size=(Dd, N))
+        A = (-idx[None, :] * s).astype(f32)
+    else:
+        raise ValueError(f"unknown a_kind {w.a_kind!r}")
+    h0 = rng.standard_normal((Bn, Dd, N), dtype=f32) if w.initial_state else None
+
+    return {
+        "io": w.io,
+        "u": _store(u, w.io),
+        "delta": _store(delta, w.io),
+        "A": np.ascontiguousarray(A),
+        "B": _store(Bm, w.io),
+        "C": _store(Cm, w.io),
+        "D": Dv,
+        "z": _store(z, w.io) if z is not None else None,
+        "delta_bias": delta_bias,
+        "h0": h0,
+    }
