@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Selective-scan forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer]
+
+A step is one call of ssm_scan_fwd (the whole forward: discretisation, scan, C
+contraction, D skip, silu gate, final state) over one batch of seeded synthetic inputs
+already resident in HBM. The default workload is a Mamba-1 layer's scan: batch 4, 2048
+channels, 16 states, 2048 steps, bf16 storage, fp32 arithmetic.
+
+Timing: W untimed warm-up calls, then exactly K calls between two device
+synchronisations; each call also sits between its own pair of HIP events on the launch
+stream. Calls rotate over several independent input/output sets whose total size is well
+above the 256 MB Infinity Cache, so every call reads HBM ("cold"). The value is the
+algorithmic bytes of K calls divided by the wall time of the timed region. One JSON line
+is printed on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
+INFINITY_CACHE_BYTES = 256 << 20
+KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernels.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"scan_fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def to_device(x, torch, device):
+    if x is None:
+        return None
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The oracle, untuned, on host cores over a bounded sample of the same workload:
+    channels 0..k-1 of the leading batch rows, all seqlen steps."""
+    import oracle
+    from ssm_workloads import widen
+
+    threads = oracle.default_threads()
+    io = inp["io"]
+
+    def sample(nb, nd):
+        sl = lambda x: None if x is None else x[:nb, :nd]
+        return (widen(sl(inp["u"]), io), widen(sl(inp["delta"]), io), inp["A"][:nd],
+                widen(inp["B"][:nb], io), widen(inp["C"][:nb], io), inp["D"][:nd],
+                widen(sl(inp["z"]), io), inp["delta_bias"][:nd], True,
+                None if inp["h0"] is None else inp["h0"][:nb, :nd])
+
+    def timed(nb, nd):
+        args = sample(nb, nd)
+        t0 = time.perf_counter()
+        oracle.scan_ref(*args, nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe_d = min(w.dim, max(threads, 16))
+    t_probe = max(timed(1, probe_d), 1e-6)
+    rows_wanted = int(budget_s / t_probe * probe_d)
+    total_rows = w.batch * w.dim
+    rows = max(probe_d, min(total_rows, rows_wanted))
+    if rows >= w.dim:
+        nb, nd = min(w.batch, rows // w.dim), w.dim
+    else:
+        nb, nd = 1, rows
+    # when the whole workload is quicker than the budget, repeat it and take the mean
+    reps = max(1, min(10, int(budget_s / max(timed(nb, nd), 1e-6)))) if rows == total_rows else 1
+    secs = sum(timed(nb, nd) for _ in range(reps)) / reps
+    sub = w.with_(batch=nb, dim=nd)
+    return {
+        "value": round(sub.algorithmic_bytes() / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"float64 sequential oracle over batch rows 0..{nb - 1}, channels "
+                   f"0..{nd - 1}, all {w.seqlen} steps ({nb * nd} of {total_rows} rows, "
+                   f"{sub.algorithmic_bytes() / 1e6:.2f} MB algorithmic), mean of {reps} run(s) "
+                   f"of {secs:.2f} s"),
+        "seconds": round(secs, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="layer")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input/output sets to rotate over (0: enough for 2x the Infinity Cache)")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true", help="skip the warm (single set) timing")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): every "
+              "(batch, channel) row of the scan is independent, so more GPUs would only "
+              "split the batch with no exchange; no multi-GPU figure is measured.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import selective_scan_fwd_amd as ssm
+    from ssm_workloads import WORKLOADS, make_inputs
+
+    if args.workload not in WORKLOADS:
+        print(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}", file=sys.stderr)
+        return 2
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w)
+    io_flag = ssm.SSM_IO_BF16 if w.io == "bf16" else ssm.SSM_IO_F32
+    flags = io_flag | ssm.SSM_DELTA_SOFTPLUS | (ssm.SSM_INITIAL_STATE if w.initial_state else 0)
+
+    base = {k: to_device(inp[k], torch, dev) for k in ("u", "delta", "B", "C", "z", "A", "D",
+                                                        "delta_bias", "h0")}
+    set_bytes = w.algorithmic_bytes()
+    nsets = args.sets or max(2, math.ceil(2 * INFINITY_CACHE_BYTES / set_bytes))
+    sets = []
+    for i in range(nsets):
+        s = {k: (v if (i == 0 or v is None) else v.clone()) for k, v in base.items()}
+        s["out"] = torch.empty_like(s["u"])
+        s["fin"] = (s["h0"].clone() if s["h0"] is not None
+                    else torch.empty((w.batch, w.dim, w.dstate), device=dev, dtype=torch.float32))
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    calls = [(ptr(s["u"]), ptr(s["delta"]), ptr(s["A"]), ptr(s["B"]), ptr(s["C"]), ptr(s["D"]),
+              ptr(s["z"]), ptr(s["delta_bias"]), flags, ptr(s["out"]), ptr(s["fin"]),
+              w.batch, w.dim, w.dstate, w.seqlen, sp) for s in sets]
+    fn = ssm.lib().ssm_scan_fwd
+
+    def launch(i):
+        st = fn(*calls[i % nsets])
+        if st != 0:
+            raise ssm.SsmScanError(st)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    warm = None
+    if not args.no_warm:
+        wk = max(20, K // 2)
+        evw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(wk)]
+        for i in range(wk):
+            evw[i][0].record(stream)
+            launch(0)
+            evw[i][1].record(stream)
+        torch.cuda.synchronize()
+        wms = np.array([a.elapsed_time(b) for a, b in evw])
+        warm = {"kernel_us_median": round(float(np.median(wms)) * 1e3, 3),
+                "GBps": round(set_bytes / (float(np.median(wms)) * 1e-3) / 1e9, 1),
+                "note": "one buffer set reused (reads may hit the Infinity Cache); not the metric"}
+
+    value = set_bytes * K / wall / 1e9
+    avg_ms = float(kern_ms.mean())
+    achieved = set_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+
+    result = {
+        "metric": "scan GB/s & % HBM peak (1 MI355X), b4 d2048 N16 L2048 bf16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64 draws, shapes and distributions of the workload)",
+        "config": {
+            "workload": w.describe(),
+            "batch": w.batch, "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen,
+            "io_dtype": w.io, "gate": w.gate, "delta_softplus": True,
+            "initial_state": w.initial_state, "buffer_sets": nsets,
+            "algorithmic_bytes": set_bytes,
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(w.elements * K / wall, 1),
+        "tuples_per_s": round(w.tuples * K / wall, 1),
+        "kernel_us": {"mean": round(avg_ms * 1e3, 3),
+                      "median": round(float(np.median(kern_ms)) * 1e3, 3),
+                      "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                      "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "scan_fwd_kernel",
+            "kernel_hash": kernel_hash(),
+        },
+        "warm": warm,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_baseline_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,116 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective-scan forward library.
+ *
+ * The operation (Mamba's selective scan, forward pass) is defined on these pages:
+ *   - ybb.press, "Mamba state-space model: from theory to production CUDA kernel
+ *     optimisation": section 1.2 (discretisation and recurrence h_t = A_bar h_{t-1} +
+ *     B_bar x_t, y_t = C h_t), section 2.3 (causal selective scan with delta-dependent
+ *     exp(delta*A) and delta*B, then the D skip), section 3.2 (the associative combine
+ *     (A1,B1) o (A2,B2) = (A2*A1, A2*B1 + B2)), section 4.2 (kernel arguments u, delta, A,
+ *     B, C, D, out, final_state with u/delta/out laid out [batch, dim, seq_len]),
+ *     section 7.1 (softplus on delta, initial state, returned final state);
+ *   - jsqmd.com, "From matrix summation to state updates: Blelloch parallel scan as the
+ *     engine of Mamba.py", section 3.2 (deltaA = exp(delta*A), deltaB = delta*B, y = hs@C
+ *     + D*x);
+ *   - mhpq.cn/news/1057127, "The hardware truth of Mamba's parallel scan", section 1
+ *     (diagonal A, independent state chains) and section 2 (one fused kernel including a
+ *     sigmoid-type gate).
+ *
+ * For every batch row b < batch, channel d < dim and state n < dstate:
+ *
+ *   dt_t     = delta[b,d,t] + delta_bias[d]         (bias optional, 0 if NULL)
+ *   dt_t     = softplus(dt_t)                       (if SSM_DELTA_SOFTPLUS)
+ *   h_t[n]   = exp(dt_t * A[d,n]) * h_{t-1}[n] + dt_t * B[b,n,t] * u[b,d,t]
+ *   y_t      = sum_n C[b,n,t] * h_t[n] + D[d] * u[b,d,t]     (D optional)
+ *   out[b,d,t] = y_t * z * sigmoid(z), z = z[b,d,t]          (gate optional: y_t if NULL)
+ *   final_state[b,d,n] = h_{L-1}[n]                          (ungated state after the last step)
+ *
+ * with h_{-1} = 0, or h_{-1} = final_state[b,d,:] on entry when SSM_INITIAL_STATE is set.
+ * softplus(x) = log(1 + exp(x)), taken as x itself above 20.
+ *
+ * Memory: every pointer is a DEVICE pointer owned by the caller; arrays are C-contiguous:
+ *   u, delta, z, out : [batch, dim, seqlen]   storage type from the flags (fp32 or bf16)
+ *   B, C             : [batch, dstate, seqlen] same storage type, shared by all channels
+ *   A                : [dim, dstate]   fp32
+ *   D, delta_bias    : [dim]           fp32
+ *   final_state      : [batch, dim, dstate] fp32
+ * Arithmetic is fp32 throughout (state, exp, accumulation); bf16 outputs are rounded to
+ * nearest-even once at the store.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream) and return
+ * once the work is queued. The library allocates nothing, keeps no per-call state, uses no
+ * atomics (results are bitwise reproducible run to run) and is safe to call from several
+ * host threads. A fault inside the kernel surfaces at the caller's next synchronisation.
+ *
+ * Every argument check happens before any HIP call, so an invalid call returns its error
+ * code without touching the device.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* flags: bits 0-1 storage type of u, delta, B, C, z and out */
+#define SSM_IO_F32 0u
+#define SSM_IO_BF16 1u
+#define SSM_IO_MASK 3u
+/* delta <- softplus(delta + delta_bias) before use */
+#define SSM_DELTA_SOFTPLUS (1u << 4)
+/* final_state is in/out: read as h_{-1}, overwritten with h_{L-1} */
+#define SSM_INITIAL_STATE (1u << 5)
+
+/* status codes */
+#define SSM_OK 0
+#define SSM_ERR_INVALID_ARG (-1) /* NULL required pointer, negative size, unknown flag bit,
+                                    SSM_INITIAL_STATE without final_state, out overlapping
+                                    an input */
+#define SSM_ERR_UNSUPPORTED (-2) /* dstate outside [1, 64], storage type not fp32/bf16,
+                                    sizes whose products overflow 64-bit offsets or whose
+                                    batch*dim or seqlen exceed 2^31 - 1 */
+#define SSM_ERR_MISALIGNED (-3)  /* a pointer not aligned to its element size */
+#define SSM_ERR_HIP (-4)         /* the HIP runtime refused the launch (no gfx950 device,
+                                    bad stream, ...) */
+
+/*
+ * ssm_scan_fwd -- the selective-scan forward described above.
+ *
+ * Required: u, delta, A, B, C, out. Optional (NULL): D (no skip), z (no gate), delta_bias
+ * (zero bias), final_state (state not returned; required with SSM_INITIAL_STATE).
+ * Sizes: batch, dim, seqlen >= 0; 1 <= dstate <= 64. batch*dim == 0 is a no-op; seqlen == 0
+ * leaves out untouched and sets final_state to the initial state (zeros unless
+ * SSM_INITIAL_STATE). Any seqlen >= 1 is supported (no multiple-of constraint); pointers
+ * need only element alignment (16-byte aligned rows take the vector path).
+ * out must not overlap u, delta, z, B, C, A, D, delta_bias or final_state.
+ * Returns SSM_OK or one of the SSM_ERR_* codes above.
+ */
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* delta_bias,
+                 uint32_t flags, void* out, float* final_state, int64_t batch, int64_t dim,
+                 int64_t dstate, int64_t seqlen, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ssm_scan_strerror(int status);
+
+/* Version of this ABI (bumped on any incompatible change). */
+int ssm_scan_abi_version(void);
+
+/*
+ * ssm_scan_debug_wave_combine -- runs only the wave-level inclusive scan of the pages'
+ * combine, (a1,b1) o (a2,b2) = (a2*a1, a2*b1 + b2) (ybb.press section 3.2; mhpq.cn/news/
+ * 1077344 section 2.2), over groups of 64 consecutive pairs, one 64-lane wavefront per
+ * group. a, b, a_out, b_out are device arrays of 64*groups floats; a_out[i], b_out[i]
+ * receive the combine of pairs 64*g .. i in order. It uses the same device routine as the
+ * forward kernel and exists so that tests can check that routine's lane wiring exactly.
+ */
+int ssm_scan_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
+                                int64_t groups, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

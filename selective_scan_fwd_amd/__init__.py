@@ -1,0 +1,162 @@
+"""Python binding of libssmscan.so, the gfx950 selective-scan forward.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels behind the C
+ABI of include/ssm_scan.h. PyTorch supplies device memory and the current stream.
+
+    out, final_state = scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                            delta_softplus=False, h0=None)
+
+``ssm_scan_fwd`` and ``ssm_scan_strerror`` are the raw C entry points (pointers as ints).
+If the library has not been built this module raises on first use; there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+from .build import LIB_PATH
+
+SSM_IO_F32 = 0
+SSM_IO_BF16 = 1
+SSM_DELTA_SOFTPLUS = 1 << 4
+SSM_INITIAL_STATE = 1 << 5
+
+SSM_OK = 0
+SSM_ERR_INVALID_ARG = -1
+SSM_ERR_UNSUPPORTED = -2
+SSM_ERR_MISALIGNED = -3
+SSM_ERR_HIP = -4
+
+EXPORTED = ("ssm_scan_fwd", "ssm_scan_strerror", "ssm_scan_abi_version",
+            "ssm_scan_debug_wave_combine")
+
+_lib = None
+
+
+class SsmScanError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"ssm_scan_fwd failed ({status}): {ssm_scan_strerror(status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssmscan.so (built in-tree by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -m selective_scan_fwd_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.ssm_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp,
+                               i64, i64, i64, i64, vp]
+    L.ssm_scan_fwd.restype = ctypes.c_int
+    L.ssm_scan_strerror.argtypes = [ctypes.c_int]
+    L.ssm_scan_strerror.restype = ctypes.c_char_p
+    L.ssm_scan_abi_version.argtypes = []
+    L.ssm_scan_abi_version.restype = ctypes.c_int
+    L.ssm_scan_debug_wave_combine.argtypes = [vp, vp, vp, vp, i64, vp]
+    L.ssm_scan_debug_wave_combine.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state,
+                 batch, dim, dstate, seqlen, stream) -> int:
+    """Raw C entry point; pointers and stream are ints (0/None for NULL)."""
+    return lib().ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state,
+                              batch, dim, dstate, seqlen, stream)
+
+
+def ssm_scan_strerror(status: int) -> str:
+    return lib().ssm_scan_strerror(status).decode()
+
+
+def ssm_scan_abi_version() -> int:
+    return lib().ssm_scan_abi_version()
+
+
+def ssm_scan_debug_wave_combine(a, b, a_out, b_out, groups, stream) -> int:
+    return lib().ssm_scan_debug_wave_combine(a, b, a_out, b_out, groups, stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_of(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
+         h0=None, out=None, final_state=None, return_final_state: bool = True
+         ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Selective-scan forward on the GPU.
+
+    u, delta, z: [batch, dim, seqlen]; B, C: [batch, dstate, seqlen] (float32 or bfloat16,
+    all the same dtype); A: [dim, dstate], D and delta_bias: [dim], h0: [batch, dim,
+    dstate] (float32). Returns (out, final_state); out has u's dtype.
+    """
+    import torch
+
+    io = u.dtype
+    if io == torch.float32:
+        flags = SSM_IO_F32
+    elif io == torch.bfloat16:
+        flags = SSM_IO_BF16
+    else:
+        raise TypeError(f"unsupported storage dtype {io}")
+    streamed = [("u", u), ("delta", delta), ("B", B), ("C", C)] + ([("z", z)] if z is not None else [])
+    for name, t in streamed:
+        if t.dtype != io:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {io}")
+    params = [("A", A)] + [(n, t) for n, t in (("D", D), ("delta_bias", delta_bias), ("h0", h0))
+                           if t is not None]
+    for name, t in params:
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    for name, t in streamed + params:
+        if not t.is_cuda or t.device != u.device:
+            raise ValueError(f"{name} must be on {u.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be [batch, dim, seqlen] and A [dim, dstate]")
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    want = {"delta": (batch, dim, seqlen), "z": (batch, dim, seqlen),
+            "B": (batch, dstate, seqlen), "C": (batch, dstate, seqlen),
+            "A": (dim, dstate), "D": (dim,), "delta_bias": (dim,), "h0": (batch, dim, dstate)}
+    for name, t in streamed + params:
+        if name in want and tuple(t.shape) != want[name]:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
+    if out is not None and (tuple(out.shape) != tuple(u.shape) or out.dtype != io
+                            or out.device != u.device or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor like u")
+    if final_state is not None and (tuple(final_state.shape) != (batch, dim, dstate)
+                                    or final_state.dtype != torch.float32
+                                    or final_state.device != u.device
+                                    or not final_state.is_contiguous()):
+        raise ValueError("final_state must be a contiguous float32 [batch, dim, dstate] tensor")
+    if out is None:
+        out = torch.empty_like(u)
+    if h0 is not None:
+        flags |= SSM_INITIAL_STATE
+        if final_state is None:
+            final_state = h0.clone()
+        elif final_state.data_ptr() != h0.data_ptr():
+            final_state.copy_(h0)
+    elif final_state is None and return_final_state:
+        final_state = torch.empty((batch, dim, dstate), device=u.device, dtype=torch.float32)
+    if delta_softplus:
+        flags |= SSM_DELTA_SOFTPLUS
+    status = ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(delta_bias), flags, _ptr(out), _ptr(final_state),
+                          batch, dim, dstate, seqlen, _stream_of(u.device))
+    if status != SSM_OK:
+        raise SsmScanError(status)
+    return out, final_state

@@ -1,0 +1,35 @@
+// Internal interface between the C-ABI layer (scan_api.cpp) and the kernels
+// (scan_kernels.hip). Not installed; the public ABI is include/ssm_scan.h.
+#pragma once
+#include <stdint.h>
+
+namespace ssm {
+
+enum class Io : int { F32 = 0, BF16 = 1 };
+
+// Everything a forward launch needs, already validated by the C-ABI layer.
+struct FwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;          // nullable
+  const void* z;           // nullable
+  const float* bias;       // nullable
+  void* out;
+  float* final_state;      // nullable unless initial_state
+  int64_t batch, dim, dstate, seqlen;
+  Io io;
+  bool softplus;
+  bool initial_state;
+  bool vec_ok;             // every row of every streamed array starts 16-byte aligned
+};
+
+// Returns a hipError_t value (0 on success).
+int launch_scan_fwd(const FwdArgs& a, void* stream);
+int launch_fill_zero(float* p, int64_t count, void* stream);
+int launch_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
+                              int64_t groups, void* stream);
+
+}  // namespace ssm

@@ -19,7 +19,7 @@ from .gen import (
     make_inputs,
     widen,
 )
-from .compare import ParityReport, parity
+from .compare import RTOL, RTOL_STATE, ParityReport, parity
 
 __all__ = [
     "WORKLOADS",
@@ -30,4 +30,6 @@ __all__ = [
     "widen",
     "parity",
     "ParityReport",
+    "RTOL",
+    "RTOL_STATE",
 ]

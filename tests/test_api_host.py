@@ -1,0 +1,109 @@
+"""Host-only checks of libssmscan.so: it loads, exports every function the public header
+declares, and rejects invalid calls with the documented status before any HIP call.
+
+No call here reaches a kernel launch: every call carries at least one invalid argument,
+so the pointers passed are never dereferenced.
+"""
+import os
+import re
+
+import pytest
+
+import selective_scan_fwd_amd as ssm
+from selective_scan_fwd_amd.build import INCLUDE
+
+HEADER = os.path.join(INCLUDE, "ssm_scan.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(ssm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert names == sorted(ssm.EXPORTED)
+    lib = ssm.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("SSM_IO_F32", "SSM_IO_BF16", "SSM_DELTA_SOFTPLUS", "SSM_INITIAL_STATE",
+                 "SSM_OK", "SSM_ERR_INVALID_ARG", "SSM_ERR_UNSUPPORTED", "SSM_ERR_MISALIGNED",
+                 "SSM_ERR_HIP"):
+        m = re.search(rf"#define {name} \(?(-?\d+)u?(?: << (\d+))?\)?", text)
+        assert m, name
+        v = int(m.group(1)) << int(m.group(2) or 0)
+        assert getattr(ssm, name) == v, name
+
+
+def test_abi_version_and_strerror():
+    assert ssm.ssm_scan_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, 17):
+        assert isinstance(ssm.ssm_scan_strerror(s), str) and ssm.ssm_scan_strerror(s)
+
+
+# fake, well-separated, 256-byte aligned addresses; never dereferenced (see module doc)
+U, DL, A, B, C, Dp, Z, BIAS, OUT, FIN = (0x100000 * (i + 1) for i in range(10))
+
+
+def call(**kw):
+    args = dict(u=U, delta=DL, A=A, B=B, C=C, D=None, z=None, delta_bias=None, flags=0,
+                out=OUT, final_state=None, batch=2, dim=4, dstate=16, seqlen=8, stream=None)
+    args.update(kw)
+    return ssm.ssm_scan_fwd(**args)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(u=None), dict(delta=None), dict(A=None), dict(B=None), dict(C=None), dict(out=None),
+    dict(batch=-1), dict(dim=-1), dict(seqlen=-1), dict(dstate=-1),
+    dict(flags=1 << 7), dict(flags=1 << 2), dict(flags=1 << 31),
+    dict(flags=ssm.SSM_INITIAL_STATE),                       # initial state without final_state
+    dict(out=U), dict(out=DL + 16), dict(out=B), dict(out=C - 8), dict(z=OUT + 4),
+    dict(final_state=OUT), dict(out=A),
+])
+def test_invalid_arguments(kw):
+    assert call(**kw) == ssm.SSM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dstate=0), dict(dstate=65), dict(dstate=1000), dict(flags=2), dict(flags=3),
+    dict(batch=1 << 40, dim=1 << 40), dict(seqlen=1 << 33), dict(batch=1 << 20, dim=1 << 12),
+])
+def test_unsupported(kw):
+    assert call(**kw) == ssm.SSM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(u=U + 2), dict(delta=DL + 1), dict(B=B + 2), dict(C=C + 3), dict(out=OUT + 2),
+    dict(z=Z + 2), dict(A=A + 2), dict(D=Dp + 1), dict(delta_bias=BIAS + 2),
+    dict(final_state=FIN + 2), dict(flags=ssm.SSM_IO_BF16, u=U + 1),
+])
+def test_misaligned(kw):
+    assert call(**kw) == ssm.SSM_ERR_MISALIGNED
+
+
+def test_empty_is_a_noop():
+    # batch * dim == 0: nothing to do and no HIP call
+    assert call(batch=0) == ssm.SSM_OK
+    assert call(dim=0) == ssm.SSM_OK
+    # seqlen == 0 with an in/out state and no output state to clear: nothing to do
+    assert call(seqlen=0, flags=ssm.SSM_INITIAL_STATE, final_state=FIN) == ssm.SSM_OK
+    assert call(seqlen=0) == ssm.SSM_OK
+
+
+def test_debug_wave_combine_validation():
+    assert ssm.ssm_scan_debug_wave_combine(None, B, C, Dp, 1, None) == ssm.SSM_ERR_INVALID_ARG
+    assert ssm.ssm_scan_debug_wave_combine(A, B, C, Dp, -1, None) == ssm.SSM_ERR_INVALID_ARG
+    assert ssm.ssm_scan_debug_wave_combine(A + 2, B, C, Dp, 1, None) == ssm.SSM_ERR_MISALIGNED
+    assert ssm.ssm_scan_debug_wave_combine(A, B, C, Dp, 0, None) == ssm.SSM_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        ssm.scan(x, x, torch.zeros(2, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
