@@ -86,7 +86,8 @@ def cpu_baseline(w, inp, budget_s: float):
         oracle.scan_ref(*args, nthreads=threads)
         return time.perf_counter() - t0
 
-    probe_d = min(w.dim, max(threads, 16))
+    timed(1, min(w.dim, threads))          # start the OpenMP thread pool outside any timing
+    probe_d = min(w.dim, max(4 * threads, 64))
     t_probe = max(timed(1, probe_d), 1e-6)
     rows_wanted = int(budget_s / t_probe * probe_d)
     total_rows = w.batch * w.dim

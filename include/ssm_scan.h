@@ -78,8 +78,9 @@ extern "C" {
 /*
  * ssm_scan_fwd -- the selective-scan forward described above.
  *
- * Required: u, delta, A, B, C, out. Optional (NULL): D (no skip), z (no gate), delta_bias
- * (zero bias), final_state (state not returned; required with SSM_INITIAL_STATE).
+ * Required: u, delta, A, B, C, out (each may be NULL only when its array is empty).
+ * Optional (NULL): D (no skip), z (no gate), delta_bias (zero bias), final_state (state not
+ * returned; required with SSM_INITIAL_STATE unless batch*dim == 0).
  * Sizes: batch, dim, seqlen >= 0; 1 <= dstate <= 64. batch*dim == 0 is a no-op; seqlen == 0
  * leaves out untouched and sets final_state to the initial state (zeros unless
  * SSM_INITIAL_STATE). Any seqlen >= 1 is supported (no multiple-of constraint); pointers

@@ -62,10 +62,8 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  int64_t dstate, int64_t seqlen, void* stream) {
   const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
   if (flags & ~known) return SSM_ERR_INVALID_ARG;
-  if (!u || !delta || !A || !B || !C || !out) return SSM_ERR_INVALID_ARG;
   if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return SSM_ERR_INVALID_ARG;
   const bool initial_state = (flags & SSM_INITIAL_STATE) != 0;
-  if (initial_state && !final_state) return SSM_ERR_INVALID_ARG;
 
   const uint32_t io = flags & SSM_IO_MASK;
   if (io != SSM_IO_F32 && io != SSM_IO_BF16) return SSM_ERR_UNSUPPORTED;
@@ -82,6 +80,11 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   if (rows > kInt32Max || seqlen > kInt32Max || dim > kInt32Max ||
       rows / 64 + 1 > kInt32Max)
     return SSM_ERR_UNSUPPORTED;
+
+  // A required array may be NULL only when it holds no element.
+  if ((elems > 0 && (!u || !delta || !out)) || (bc > 0 && (!B || !C)) || (a_elems > 0 && !A))
+    return SSM_ERR_INVALID_ARG;
+  if (initial_state && state > 0 && !final_state) return SSM_ERR_INVALID_ARG;
 
   const uintptr_t ea = static_cast<uintptr_t>(esz);
   if (!aligned(u, ea) || !aligned(delta, ea) || !aligned(B, ea) || !aligned(C, ea) ||

@@ -109,12 +109,12 @@ def test_delta_zero_zero_input_and_skip_only():
     w = WORKLOADS["tiny"].with_(batch=2, dim=8, seqlen=300, initial_state=True, seed=32)
     announce(w.describe() + " special cases")
     inp = make_inputs(w)
-    # delta = 0 without softplus: the state never moves
+    # delta = 0 with no bias and no softplus: the state never moves
     z0 = dict(inp, delta=np.zeros_like(inp["delta"]))
-    out, fin = run_hip(z0, softplus=False)
+    out, fin = run_hip(z0, softplus=False, use_bias=False)
     assert np.array_equal(fin, inp["h0"].astype(np.float64))
     ref_out, _ = oracle.scan_ref(widen(z0["u"], "f32"), np.zeros(z0["u"].shape), z0["A"],
-                                 z0["B"], z0["C"], z0["D"], None, z0["delta_bias"], False, z0["h0"])
+                                 z0["B"], z0["C"], z0["D"], None, None, False, z0["h0"])
     assert parity(out, ref_out, RTOL["f32"]).ok
     # zero input from a zero state: exactly zero everywhere
     zz = dict(inp, u=np.zeros_like(inp["u"]), h0=None)

@@ -74,11 +74,12 @@ def test_parity_optional_inputs(variant, io):
               use_bias=variant not in ("no_bias", "bare"),
               softplus=variant not in ("no_softplus", "bare"))
     if not kw["softplus"]:
-        # without softplus the step size must already be positive
+        # without softplus, delta + bias is the step size itself: keep both positive
         raw = widen(inp["delta"], io)
         pos = np.abs(raw) * 0.05 + 1e-3
         inp["delta"] = (pos.astype(np.float32) if io == "f32"
                         else f32_to_bf16_bits(pos.astype(np.float32)))
+        inp["delta_bias"] = np.abs(inp["delta_bias"]) * np.float32(0.01)
     got = run_hip(inp, **kw)
     ref = oracle_full(inp, **kw)
     assert_parity(io, *got, *ref, f"{w.describe()} {variant}")
