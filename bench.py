@@ -31,6 +31,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
+# ALU roofline. MI355X: 256 CUs x 4 SIMDs, 2.4 GHz; the fp32 vector peak of 157.3 TFLOP/s
+# is 32 fp32 FMA lanes per SIMD per clock (a wave64 VALU instruction issues in 2 clocks);
+# transcendentals (v_exp_f32) run at a quarter of that rate. The exact method needs, per
+# (batch, channel, state, step) update: dt*A (mul), exp, (dt*u)*B (mul), h = dA*h + dBu
+# (fma), y += C*h (fma): 4 VALU issue slots plus one exp = 4 more slots. Counting each
+# slot as one FMA (2 flop), an update is 16 flop-equivalents against the 157.3 peak.
+ALU_PEAK_TFLOPS = 157.3
+FLOP_EQ_PER_UPDATE = 16
 INFINITY_CACHE_BYTES = 256 << 20
 KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernels.hip"]
 
@@ -97,7 +105,7 @@ def cpu_baseline(w, inp, budget_s: float):
     else:
         nb, nd = 1, rows
     # when the whole workload is quicker than the budget, repeat it and take the mean
-    reps = max(1, min(10, int(budget_s / max(timed(nb, nd), 1e-6)))) if rows == total_rows else 1
+    reps = max(1, min(500, int(budget_s / max(timed(nb, nd), 1e-6)))) if rows == total_rows else 1
     secs = sum(timed(nb, nd) for _ in range(reps)) / reps
     sub = w.with_(batch=nb, dim=nd)
     return {
@@ -113,6 +121,30 @@ def cpu_baseline(w, inp, budget_s: float):
     }
 
 
+def copy_probe(torch, steps: int, warmup: int) -> int:
+    """Plain copy of 1 GiB between two device buffers (torch's copy kernel): reads 1 GiB and
+    writes 1 GiB per call."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n,
+                      "kernel_us_median": round(float(np.median(ms)) * 1e3, 2),
+                      "GBps_read_plus_write": round(2 * n / (float(np.median(ms)) * 1e-3) / 1e9, 1)}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +156,9 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the warm (single set) timing")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy instead (HBM reference, and "
+                         "the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -135,6 +170,9 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_probe:
+        return copy_probe(torch, args.steps, args.warmup)
 
     import selective_scan_fwd_amd as ssm
     from ssm_workloads import WORKLOADS, make_inputs
@@ -211,6 +249,7 @@ def main() -> int:
     value = set_bytes * K / wall / 1e9
     avg_ms = float(kern_ms.mean())
     achieved = set_bytes / (avg_ms * 1e-3) / 1e9
+    alu_achieved = FLOP_EQ_PER_UPDATE * w.tuples / (avg_ms * 1e-3) / 1e12
     traffic = load_traffic(args.workload)
 
     result = {
@@ -241,14 +280,20 @@ def main() -> int:
                       "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                       "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bound": "alu",
+            "achieved": round(alu_achieved, 3),
+            "peak": ALU_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(alu_achieved / ALU_PEAK_TFLOPS, 4),
             "traffic": traffic,
             "kernel": "scan_fwd_kernel",
             "kernel_hash": kernel_hash(),
+            "work": (f"{FLOP_EQ_PER_UPDATE} flop-equivalents per (b,d,n,t) update (2 mul + 2 fma "
+                     "+ 1 exp at quarter rate = 8 FMA issue slots) x "
+                     f"{w.tuples} updates per launch"),
+            "hbm": {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "bytes": f"{set_bytes} algorithmic bytes per launch"},
         },
         "warm": warm,
     }

@@ -69,8 +69,10 @@ extern "C" {
                                     SSM_INITIAL_STATE without final_state, out overlapping
                                     an input */
 #define SSM_ERR_UNSUPPORTED (-2) /* dstate outside [1, 64], storage type not fp32/bf16,
-                                    sizes whose products overflow 64-bit offsets or whose
-                                    batch*dim or seqlen exceed 2^31 - 1 */
+                                    sizes whose products overflow 64-bit offsets, batch*dim
+                                    or seqlen above 2^31 - 1, or one row (seqlen elements)
+                                    or one batch row of B (dstate*seqlen elements) above
+                                    2 GiB */
 #define SSM_ERR_MISALIGNED (-3)  /* a pointer not aligned to its element size */
 #define SSM_ERR_HIP (-4)         /* the HIP runtime refused the launch (no gfx950 device,
                                     bad stream, ...) */

@@ -80,6 +80,10 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   if (rows > kInt32Max || seqlen > kInt32Max || dim > kInt32Max ||
       rows / 64 + 1 > kInt32Max)
     return SSM_ERR_UNSUPPORTED;
+  // Rows of u/delta/z/out and each batch row's B/C block are addressed with 32-bit byte
+  // offsets (with one chunk of slack past the end).
+  if (seqlen * esz > (int64_t(1) << 31) || dstate * seqlen * esz > (int64_t(1) << 31))
+    return SSM_ERR_UNSUPPORTED;
 
   // A required array may be NULL only when it holds no element.
   if ((elems > 0 && (!u || !delta || !out)) || (bc > 0 && (!B || !C)) || (a_elems > 0 && !A))
