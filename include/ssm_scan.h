@@ -54,6 +54,13 @@
 extern "C" {
 #endif
 
+/* Exported from libssmscan.so (built with hidden visibility for everything else). */
+#if defined(__GNUC__) || defined(__clang__)
+#define SSM_API __attribute__((visibility("default")))
+#else
+#define SSM_API
+#endif
+
 /* flags: bits 0-1 storage type of u, delta, B, C, z and out */
 #define SSM_IO_F32 0u
 #define SSM_IO_BF16 1u
@@ -85,21 +92,23 @@ extern "C" {
  * returned; required with SSM_INITIAL_STATE unless batch*dim == 0).
  * Sizes: batch, dim, seqlen >= 0; 1 <= dstate <= 64. batch*dim == 0 is a no-op; seqlen == 0
  * leaves out untouched and sets final_state to the initial state (zeros unless
- * SSM_INITIAL_STATE). Any seqlen >= 1 is supported (no multiple-of constraint); pointers
+ * SSM_INITIAL_STATE). Any seqlen >= 1 is supported (no multiple-of constraint). Up to 32
+ * steps run a per-step kernel (decode, state passing), longer sequences the chunked scan;
+ * the two agree to fp32 rounding, not bitwise. Pointers
  * need only element alignment (16-byte aligned rows take the vector path).
  * out must not overlap u, delta, z, B, C, A, D, delta_bias or final_state.
  * Returns SSM_OK or one of the SSM_ERR_* codes above.
  */
-int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+SSM_API int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* delta_bias,
                  uint32_t flags, void* out, float* final_state, int64_t batch, int64_t dim,
                  int64_t dstate, int64_t seqlen, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
-const char* ssm_scan_strerror(int status);
+SSM_API const char* ssm_scan_strerror(int status);
 
 /* Version of this ABI (bumped on any incompatible change). */
-int ssm_scan_abi_version(void);
+SSM_API int ssm_scan_abi_version(void);
 
 /*
  * ssm_scan_debug_wave_combine -- runs only the wave-level inclusive scan of the pages'
@@ -109,7 +118,7 @@ int ssm_scan_abi_version(void);
  * receive the combine of pairs 64*g .. i in order. It uses the same device routine as the
  * forward kernel and exists so that tests can check that routine's lane wiring exactly.
  */
-int ssm_scan_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
+SSM_API int ssm_scan_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
                                 int64_t groups, void* stream);
 
 #ifdef __cplusplus

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libssmscan.so")
-SOURCES = ["scan_kernels.hip", "scan_api.cpp"]
+SOURCES = ["scan_kernels.hip", "scan_short.hip", "scan_api.cpp"]
 ARCH = "gfx950"
 
 
@@ -29,7 +29,7 @@ def hipcc() -> str:
 def compile_flags() -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-I", INCLUDE, "-I", CSRC]
+            "-fvisibility=hidden", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 
 def build(verbose: bool = False) -> str:

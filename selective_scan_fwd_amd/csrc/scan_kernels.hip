@@ -41,49 +41,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_math.h"
 #include "scan_launch.h"
 
 namespace ssm {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
-__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
-
 __device__ __forceinline__ float readlane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// softplus(x) = max(x, 0) + log1p(e), e = exp(-|x|) in (0, 1]. With w = fl(1 + e), the
-// rounding error d = (w - 1) - e is exact (w - 1 is exact for w in [1, 2], and the error of
-// a rounded sum is representable), and log1p(e) = log(w) - d / w + O(d^2); replacing d / w
-// by d changes the result by d * e / (1 + e), below 1e-7 relative since log1p(e) >= e ln 2.
-// When w rounds to 1, the result is e exactly. Two transcendentals (exp2, log2).
-__device__ __forceinline__ float softplus_f(float x) {
-  const float e = exp2_hw(-__builtin_fabsf(x) * kLog2e);
-  const float w = 1.0f + e;
-  const float err = (w - 1.0f) - e;
-  return __builtin_fmaxf(x, 0.0f) + __builtin_fmaf(log2_hw(w), kLn2, -err);
-}
-
-// y * silu(z) = y * z / (1 + e^-z)
-__device__ __forceinline__ float gate_f(float y, float z) {
-  return y * z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
-}
-
-// ---------------------------------------------------------------- storage types
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Round to bf16, nearest-even (v_cvt_pk_bf16_f32 on gfx950), two values per dword.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 l = (__bf16)lo, h = (__bf16)hi;
-  return uint32_t(__builtin_bit_cast(uint16_t, l)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, h)) << 16);
 }
 
 // Elements per 16-byte access.
@@ -382,6 +347,9 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
           *base = __builtin_bit_cast(float4, raw[k]);
         }
       }
+      // Consume the word on every path, so the load is waited for here even by lanes with
+      // nothing to store, and no wait for it is left pending into the next stage.
+      asm volatile("" ::"v"(raw[k].x));
     }
   };
 
@@ -520,11 +488,26 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
         // that covers them is the commit of the next group.
         if constexpr (kDmaInputs) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         load_inputs(c + 1);
+        asm volatile("" ::: "memory");  // the DMA stays ahead of the z loads below
       }
       if (g == n_groups - 1) load_z(c);
       if (active) compute_group(it, g);
       stage_commit((it + 1) & 1);
-      __syncthreads();
+      if constexpr (kDmaInputs) {
+        // A bare s_barrier: with a release fence the compiler would wait for the DMA of the
+        // next chunk's u and delta at the first barrier after it is issued, exposing its
+        // latency once per chunk. The DMA writes only this wave's own lds_in slot, read
+        // after the chunk's last barrier, so it only has to land by then: at the last
+        // group every VMEM operation but the z loads issued after it must have completed.
+        // Commits are LDS writes, complete before every barrier.
+        if (g == n_groups - 1) {
+          if (p.z) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlocks) : "memory");
+          else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      } else {
+        __syncthreads();
+      }
     }
 
     if (p.z) {
@@ -618,6 +601,10 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
 #endif
 
 int launch_scan_fwd(const FwdArgs& a, void* stream) {
+  return a.seqlen <= kShortMaxSeqlen ? launch_scan_short(a, stream) : launch_scan_chunked(a, stream);
+}
+
+int launch_scan_chunked(const FwdArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.io == Io::BF16) return launch_typed<uint16_t, SSM_BF16_T, SSM_BF16_K, SSM_BF16_G, SSM_BF16_DMA>(a, s);
   return launch_typed<float, SSM_F32_T, SSM_F32_K, SSM_F32_G, SSM_F32_DMA>(a, s);

@@ -26,8 +26,17 @@ struct FwdArgs {
   bool vec_ok;             // every row of every streamed array starts 16-byte aligned
 };
 
-// Returns a hipError_t value (0 on success).
-int launch_scan_fwd(const FwdArgs& a, void* stream);
+// Sequences of at most this many steps take the short-sequence kernel (one lane per
+// channel and state, stepping through time); longer ones the chunked scan kernel.
+#ifndef SSM_SHORT_MAX_L
+#define SSM_SHORT_MAX_L 32
+#endif
+constexpr int64_t kShortMaxSeqlen = SSM_SHORT_MAX_L;
+
+// Each returns a hipError_t value (0 on success).
+int launch_scan_fwd(const FwdArgs& a, void* stream);    // dispatches on seqlen
+int launch_scan_short(const FwdArgs& a, void* stream);  // short-sequence kernel
+int launch_scan_chunked(const FwdArgs& a, void* stream);  // chunked scan kernel
 int launch_fill_zero(float* p, int64_t count, void* stream);
 int launch_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
                               int64_t groups, void* stream);

@@ -18,7 +18,7 @@ HEADER = os.path.join(INCLUDE, "ssm_scan.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(ssm_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:SSM_API\s+)?(?:const\s+)?\w+\**\s+\**(ssm_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_function():
@@ -27,6 +27,21 @@ def test_exports_every_declared_function():
     lib = ssm.lib()
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_exports_nothing_else():
+    """Only the C ABI is visible: no C++ internals leak out of the library."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    from selective_scan_fwd_amd.build import LIB_PATH
+    out = subprocess.run([nm, "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    text_syms = sorted(line.split()[-1] for line in out.splitlines()
+                       if len(line.split()) == 3 and line.split()[1] == "T")
+    assert text_syms == declared_functions()
 
 
 def test_header_constants_match_binding():
