@@ -6,7 +6,8 @@ imports nothing from the GPU package.
 
 ``scan_ref`` runs the float64 sequential definition in ``ssm_ref.c`` over whole
 tensors; ``scan_rows`` runs it on selected (batch, channel) rows of a large workload,
-widening only the slices those rows read.
+widening only the slices those rows read. ``scan_bwd_ref`` runs the reverse-mode
+derivative of that definition (``ssm_ref_bwd.c``).
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssmref.so")
-_SOURCES = ["ssm_ref.c"]
+_SOURCES = ["ssm_ref.c", "ssm_ref_bwd.c"]
 _lib = None
 
 
@@ -54,6 +55,12 @@ def _load():
                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                        ctypes.c_int]
         fn.restype = ctypes.c_int
+    p = ctypes.POINTER(ctypes.c_double)
+    fn = lib.ssm_ref_scan_bwd_f64
+    fn.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_int, p, p, p,
+                   p, p, p, p, p, p, p, p, p,
+                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    fn.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -102,6 +109,43 @@ def scan_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
     return out, fin
+
+
+def scan_bwd_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                 h0=None, dout=None, dfinal=None, nthreads: Optional[int] = None
+                 ) -> Dict[str, Optional[np.ndarray]]:
+    """Gradients of L = sum(dout * out) + sum(dfinal * final_state) with respect to every
+    input of ``scan_ref`` (float64). Returns a dict with du, ddelta [B,D,L], dA [D,N],
+    dB, dC [B,N,L], dD [D] (None without D), dz [B,D,L] (None without z), dbias [D]
+    (None without a bias) and dh0 [B,D,N] (the gradient with respect to the initial
+    state, zero or given)."""
+    lib = _load()
+    f64 = lambda x: None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+    u, delta, A, B, C, D, z, delta_bias, h0, dout, dfinal = map(
+        f64, (u, delta, A, B, C, D, z, delta_bias, h0, dout, dfinal))
+    batch, dim, seqlen = u.shape
+    dstate = A.shape[1]
+    if delta.shape != u.shape or A.shape != (dim, dstate) or B.shape != (batch, dstate, seqlen) \
+            or C.shape != B.shape or dout is None or dout.shape != u.shape:
+        raise ValueError("oracle: inconsistent shapes")
+    if dfinal is not None and dfinal.shape != (batch, dim, dstate):
+        raise ValueError("oracle: dfinal shape")
+    g = {"du": np.empty_like(u), "ddelta": np.empty_like(u), "dA": np.empty_like(A),
+         "dB": np.empty_like(B), "dC": np.empty_like(C),
+         "dD": None if D is None else np.empty_like(D),
+         "dz": None if z is None else np.empty_like(z),
+         "dbias": None if delta_bias is None else np.empty_like(delta_bias),
+         "dh0": np.empty((batch, dim, dstate))}
+    ptr = lambda x: None if x is None else x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    rc = lib.ssm_ref_scan_bwd_f64(
+        ptr(u), ptr(delta), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z), ptr(delta_bias),
+        1 if delta_softplus else 0, ptr(h0), ptr(dout), ptr(dfinal),
+        ptr(g["du"]), ptr(g["ddelta"]), ptr(g["dA"]), ptr(g["dB"]), ptr(g["dC"]),
+        ptr(g["dD"]), ptr(g["dz"]), ptr(g["dbias"]), ptr(g["dh0"]),
+        batch, dim, dstate, seqlen, int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle backward returned {rc}")
+    return g
 
 
 def _widen(x, io):

@@ -28,6 +28,19 @@ int ssm_ref_scan_f32(const float* u, const float* delta, const float* A, const f
                      float* out, float* final_state, int64_t batch, int64_t dim,
                      int64_t dstate, int64_t seqlen, int nthreads);
 
+/* Reverse-mode derivative of ssm_ref_scan_f64 for the loss
+ * sum(dout * out) + sum(dfinal * final_state) (ssm_ref_bwd.c).
+ *   dout [batch, dim, seqlen] required; dfinal [batch, dim, dstate] may be NULL (zero).
+ *   du, ddelta [batch, dim, seqlen], dA [dim, dstate], dB, dC [batch, dstate, seqlen]
+ *   required; dz required when z is given; dD, dbias, dh0 may be NULL (not returned). */
+int ssm_ref_scan_bwd_f64(const double* u, const double* delta, const double* A,
+                         const double* B, const double* C, const double* D, const double* z,
+                         const double* delta_bias, int delta_softplus, const double* h0,
+                         const double* dout, const double* dfinal, double* du,
+                         double* ddelta, double* dA, double* dB, double* dC, double* dD,
+                         double* dz, double* dbias, double* dh0, int64_t batch, int64_t dim,
+                         int64_t dstate, int64_t seqlen, int nthreads);
+
 int ssm_ref_abi_version(void);
 
 #ifdef __cplusplus
