@@ -104,6 +104,65 @@ SSM_API int ssm_scan_fwd(const void* u, const void* delta, const float* A, const
                  uint32_t flags, void* out, float* final_state, int64_t batch, int64_t dim,
                  int64_t dstate, int64_t seqlen, void* stream);
 
+/*
+ * Training: the forward that also saves states, and the backward pass.
+ *
+ * The backward recomputes the scan from states the forward saved at regular intervals,
+ * instead of keeping every h_t: mhpq.cn/news/1077344 (section 3.3) describes the fused
+ * scan's backward this way (only chunk-boundary states are stored; the scan is run again
+ * from them inside the kernel before the gradients are formed).
+ */
+
+/* Saved states sit every SSM_CKPT_INTERVAL steps: entry k is the state entering step
+ * k * SSM_CKPT_INTERVAL (entry 0 is the initial state). */
+#define SSM_CKPT_INTERVAL 512
+
+/* Number of saved states per (batch row, channel): ceil(seqlen / SSM_CKPT_INTERVAL), 0 for
+ * seqlen <= 0. */
+SSM_API int64_t ssm_scan_ckpt_count(int64_t seqlen);
+
+/*
+ * ssm_scan_fwd_ckpt -- ssm_scan_fwd that also writes the saved states.
+ * chunk_states: fp32 [batch, dim, ssm_scan_ckpt_count(seqlen), dstate], device, written
+ * (required unless empty; must not overlap out). Every other argument and error code is
+ * that of ssm_scan_fwd, whose outputs it produces bit for bit.
+ */
+SSM_API int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                              const void* C, const float* D, const void* z,
+                              const float* delta_bias, uint32_t flags, void* out,
+                              float* final_state, float* chunk_states, int64_t batch,
+                              int64_t dim, int64_t dstate, int64_t seqlen, void* stream);
+
+/*
+ * ssm_scan_bwd -- gradients of L = sum(dout * out) + sum(dfinal * final_state) with
+ * respect to every input of ssm_scan_fwd.
+ *
+ * Inputs: the forward's u, delta, A, B, C, D, z, delta_bias and flags (SSM_INITIAL_STATE
+ * is accepted and has no further effect: the initial state is entry 0 of chunk_states),
+ * chunk_states from ssm_scan_fwd_ckpt on the same inputs, dout [batch, dim, seqlen] in the
+ * storage type, dfinal fp32 [batch, dim, dstate] (NULL: zero).
+ * Outputs (device, written; the "summed" ones are overwritten, not accumulated into):
+ *   du, ddelta   [batch, dim, seqlen]  storage type (ddelta is the gradient of the raw
+ *                delta, through softplus when SSM_DELTA_SOFTPLUS is set)
+ *   dz           [batch, dim, seqlen]  storage type; required when z is given, else unused
+ *   dA           [dim, dstate]         fp32, summed over batch rows
+ *   dB, dC       [batch, dstate, seqlen] fp32, summed over channels
+ *   dD, dbias    [dim]                 fp32, summed over batch rows and steps; NULL = not
+ *                wanted (ignored when D or delta_bias is NULL)
+ *   dh0          [batch, dim, dstate]  fp32, gradient of the initial state; NULL = not
+ *                wanted
+ * The summed gradients are accumulated with floating-point atomics, so they are not
+ * bitwise reproducible from run to run (within fp32 rounding of one another); du, ddelta,
+ * dz and dh0 are. Scratch: none beyond LDS. Errors as for ssm_scan_fwd.
+ */
+SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                         const void* C, const float* D, const void* z,
+                         const float* delta_bias, uint32_t flags, const float* chunk_states,
+                         const void* dout, const float* dfinal, void* du, void* ddelta,
+                         float* dA, float* dB, float* dC, float* dD, void* dz, float* dbias,
+                         float* dh0, int64_t batch, int64_t dim, int64_t dstate,
+                         int64_t seqlen, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 SSM_API const char* ssm_scan_strerror(int status);
 

@@ -1,20 +1,22 @@
-"""Python binding of libssmscan.so, the gfx950 selective-scan forward.
+"""Python binding of libssmscan.so, the gfx950 selective-scan forward and backward.
 
 Argument marshalling only: every step of the scan runs in the HIP kernels behind the C
 ABI of include/ssm_scan.h. PyTorch supplies device memory and the current stream.
 
     out, final_state = scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                             delta_softplus=False, h0=None)
+    out, final_state, chunk_states = scan_train(...same arguments...)
+    grads = scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None,
+                          delta_bias=None, delta_softplus=False, dfinal=None)
 
-``ssm_scan_fwd`` and ``ssm_scan_strerror`` are the raw C entry points (pointers as ints).
-If the library has not been built this module raises on first use; there is no CPU
-fallback.
+The ``ssm_scan_*`` functions are the raw C entry points (pointers as ints). If the
+library has not been built this module raises on first use; there is no CPU fallback.
 """
 from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import Dict, Optional, Tuple
 
 from .build import LIB_PATH
 
@@ -29,15 +31,18 @@ SSM_ERR_UNSUPPORTED = -2
 SSM_ERR_MISALIGNED = -3
 SSM_ERR_HIP = -4
 
+SSM_CKPT_INTERVAL = 512
+
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_strerror", "ssm_scan_abi_version",
-            "ssm_scan_debug_wave_combine")
+            "ssm_scan_debug_wave_combine", "ssm_scan_ckpt_count", "ssm_scan_fwd_ckpt",
+            "ssm_scan_bwd")
 
 _lib = None
 
 
 class SsmScanError(RuntimeError):
     def __init__(self, status: int):
-        super().__init__(f"ssm_scan_fwd failed ({status}): {ssm_scan_strerror(status)}")
+        super().__init__(f"ssm_scan call failed ({status}): {ssm_scan_strerror(status)}")
         self.status = status
 
 
@@ -60,6 +65,14 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_abi_version.restype = ctypes.c_int
     L.ssm_scan_debug_wave_combine.argtypes = [vp, vp, vp, vp, i64, vp]
     L.ssm_scan_debug_wave_combine.restype = ctypes.c_int
+    L.ssm_scan_ckpt_count.argtypes = [i64]
+    L.ssm_scan_ckpt_count.restype = i64
+    L.ssm_scan_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
+                                    i64, i64, i64, i64, vp]
+    L.ssm_scan_fwd_ckpt.restype = ctypes.c_int
+    L.ssm_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
+                               vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+    L.ssm_scan_bwd.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -69,6 +82,24 @@ def ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state,
     """Raw C entry point; pointers and stream are ints (0/None for NULL)."""
     return lib().ssm_scan_fwd(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state,
                               batch, dim, dstate, seqlen, stream)
+
+
+def ssm_scan_fwd_ckpt(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state,
+                      chunk_states, batch, dim, dstate, seqlen, stream) -> int:
+    return lib().ssm_scan_fwd_ckpt(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state,
+                                   chunk_states, batch, dim, dstate, seqlen, stream)
+
+
+def ssm_scan_ckpt_count(seqlen: int) -> int:
+    return lib().ssm_scan_ckpt_count(seqlen)
+
+
+def ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, flags, chunk_states, dout, dfinal,
+                 du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch, dim, dstate, seqlen,
+                 stream) -> int:
+    return lib().ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, flags, chunk_states, dout,
+                              dfinal, du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch, dim,
+                              dstate, seqlen, stream)
 
 
 def ssm_scan_strerror(status: int) -> str:
@@ -92,15 +123,8 @@ def _stream_of(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
-         h0=None, out=None, final_state=None, return_final_state: bool = True
-         ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
-    """Selective-scan forward on the GPU.
-
-    u, delta, z: [batch, dim, seqlen]; B, C: [batch, dstate, seqlen] (float32 or bfloat16,
-    all the same dtype); A: [dim, dstate], D and delta_bias: [dim], h0: [batch, dim,
-    dstate] (float32). Returns (out, final_state); out has u's dtype.
-    """
+def _check(u, delta, A, B, C, D, z, delta_bias, h0):
+    """Dtype, device, contiguity and shape checks; returns (flags, batch, dim, dstate, seqlen)."""
     import torch
 
     io = u.dtype
@@ -134,6 +158,15 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: boo
     for name, t in streamed + params:
         if name in want and tuple(t.shape) != want[name]:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
+    return flags, batch, dim, dstate, seqlen
+
+
+def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final_state,
+             return_final_state, save_states):
+    import torch
+
+    flags, batch, dim, dstate, seqlen = _check(u, delta, A, B, C, D, z, delta_bias, h0)
+    io = u.dtype
     if out is not None and (tuple(out.shape) != tuple(u.shape) or out.dtype != io
                             or out.device != u.device or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor like u")
@@ -154,9 +187,80 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: boo
         final_state = torch.empty((batch, dim, dstate), device=u.device, dtype=torch.float32)
     if delta_softplus:
         flags |= SSM_DELTA_SOFTPLUS
-    status = ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), flags, _ptr(out), _ptr(final_state),
-                          batch, dim, dstate, seqlen, _stream_of(u.device))
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            flags, _ptr(out), _ptr(final_state))
+    sizes = (batch, dim, dstate, seqlen, _stream_of(u.device))
+    states = None
+    if save_states:
+        states = torch.empty((batch, dim, ssm_scan_ckpt_count(seqlen), dstate), device=u.device,
+                             dtype=torch.float32)
+        status = ssm_scan_fwd_ckpt(*args, _ptr(states), *sizes)
+    else:
+        status = ssm_scan_fwd(*args, *sizes)
     if status != SSM_OK:
         raise SsmScanError(status)
-    return out, final_state
+    return out, final_state, states
+
+
+def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
+         h0=None, out=None, final_state=None, return_final_state: bool = True
+         ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Selective-scan forward on the GPU.
+
+    u, delta, z: [batch, dim, seqlen]; B, C: [batch, dstate, seqlen] (float32 or bfloat16,
+    all the same dtype); A: [dim, dstate], D and delta_bias: [dim], h0: [batch, dim,
+    dstate] (float32). Returns (out, final_state); out has u's dtype.
+    """
+    out, fin, _ = _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out,
+                           final_state, return_final_state, False)
+    return out, fin
+
+
+def scan_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
+               h0=None):
+    """``scan`` that also returns the states the backward pass restarts from:
+    (out, final_state, chunk_states [batch, dim, ceil(seqlen / 512), dstate] float32)."""
+    return _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, None, None, True,
+                    True)
+
+
+def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_bias=None,
+                  delta_softplus: bool = False, dfinal=None, want_dh0: bool = True
+                  ) -> Dict[str, Optional["torch.Tensor"]]:
+    """Gradients of sum(dout * out) + sum(dfinal * final_state) for the forward on the same
+    inputs. Returns du, ddelta, dz (u's dtype), dA, dB, dC, dD, dbias, dh0 (float32; None
+    where the input is absent or, for dh0, not wanted)."""
+    import torch
+
+    flags, batch, dim, dstate, seqlen = _check(u, delta, A, B, C, D, z, delta_bias, None)
+    n_ck = ssm_scan_ckpt_count(seqlen)
+    if (tuple(chunk_states.shape) != (batch, dim, n_ck, dstate)
+            or chunk_states.dtype != torch.float32 or not chunk_states.is_contiguous()
+            or chunk_states.device != u.device):
+        raise ValueError(f"chunk_states must be float32 {(batch, dim, n_ck, dstate)}")
+    if tuple(dout.shape) != tuple(u.shape) or dout.dtype != u.dtype or not dout.is_contiguous() \
+            or dout.device != u.device:
+        raise ValueError("dout must be a contiguous tensor like u")
+    if dfinal is not None and (tuple(dfinal.shape) != (batch, dim, dstate)
+                               or dfinal.dtype != torch.float32 or not dfinal.is_contiguous()
+                               or dfinal.device != u.device):
+        raise ValueError("dfinal must be a contiguous float32 [batch, dim, dstate] tensor")
+    if delta_softplus:
+        flags |= SSM_DELTA_SOFTPLUS
+    dev = u.device
+    f32 = dict(device=dev, dtype=torch.float32)
+    g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+         "dz": None if z is None else torch.empty_like(u),
+         "dA": torch.empty((dim, dstate), **f32), "dB": torch.empty((batch, dstate, seqlen), **f32),
+         "dC": torch.empty((batch, dstate, seqlen), **f32),
+         "dD": None if D is None else torch.empty((dim,), **f32),
+         "dbias": None if delta_bias is None else torch.empty((dim,), **f32),
+         "dh0": torch.empty((batch, dim, dstate), **f32) if want_dh0 else None}
+    status = ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(delta_bias), flags, _ptr(chunk_states), _ptr(dout), _ptr(dfinal),
+                          _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                          _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dbias"]),
+                          _ptr(g["dh0"]), batch, dim, dstate, seqlen, _stream_of(dev))
+    if status != SSM_OK:
+        raise SsmScanError(status)
+    return g

@@ -1,6 +1,7 @@
 // C-ABI entry points of libssmscan.so (declared in include/ssm_scan.h).
 // Argument checking happens here, before any HIP call; the launches are in
 // scan_kernels.hip.
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -56,10 +57,18 @@ const char* ssm_scan_strerror(int status) {
   }
 }
 
-int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
-                 const void* C, const float* D, const void* z, const float* delta_bias,
-                 uint32_t flags, void* out, float* final_state, int64_t batch, int64_t dim,
-                 int64_t dstate, int64_t seqlen, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int64_t ckpt_count(int64_t seqlen) {
+  return seqlen <= 0 ? 0 : (seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
+}
+
+int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+             const float* D, const void* z, const float* delta_bias, uint32_t flags, void* out,
+             float* final_state, float* ckpt, bool want_ckpt, int64_t batch, int64_t dim,
+             int64_t dstate, int64_t seqlen, void* stream) {
   const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
   if (flags & ~known) return SSM_ERR_INVALID_ARG;
   if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return SSM_ERR_INVALID_ARG;
@@ -89,6 +98,13 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   if ((elems > 0 && (!u || !delta || !out)) || (bc > 0 && (!B || !C)) || (a_elems > 0 && !A))
     return SSM_ERR_INVALID_ARG;
   if (initial_state && state > 0 && !final_state) return SSM_ERR_INVALID_ARG;
+  int64_t ckpt_elems = 0, ckpt_bytes = 0;
+  if (want_ckpt) {
+    if (!mul_ok(state, ckpt_count(seqlen), &ckpt_elems) || !mul_ok(ckpt_elems, 4, &ckpt_bytes))
+      return SSM_ERR_UNSUPPORTED;
+    if (ckpt_elems > 0 && !ckpt) return SSM_ERR_INVALID_ARG;
+    if (!aligned(ckpt, 4)) return SSM_ERR_MISALIGNED;
+  }
 
   const uintptr_t ea = static_cast<uintptr_t>(esz);
   if (!aligned(u, ea) || !aligned(delta, ea) || !aligned(B, ea) || !aligned(C, ea) ||
@@ -104,7 +120,8 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
         overlaps(o, span(C, bc_bytes)) || overlaps(o, span(A, a_elems * 4)) ||
         (D && overlaps(o, span(D, dim * 4))) ||
         (delta_bias && overlaps(o, span(delta_bias, dim * 4))) ||
-        (final_state && overlaps(o, span(final_state, state_bytes))))
+        (final_state && overlaps(o, span(final_state, state_bytes))) ||
+        (ckpt_bytes > 0 && overlaps(o, span(ckpt, ckpt_bytes))))
       return SSM_ERR_INVALID_ARG;
   }
 
@@ -136,7 +153,130 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
   a.initial_state = initial_state;
   a.vec_ok = ((seqlen * esz) % 16 == 0) && aligned(u, 16) && aligned(delta, 16) &&
              aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16));
+  a.ckpt = want_ckpt ? ckpt : nullptr;
   return ssm::launch_scan_fwd(a, stream) == 0 ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* delta_bias,
+                 uint32_t flags, void* out, float* final_state, int64_t batch, int64_t dim,
+                 int64_t dstate, int64_t seqlen, void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state, nullptr, false,
+                  batch, dim, dstate, seqlen, stream);
+}
+
+int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      uint32_t flags, void* out, float* final_state, float* chunk_states,
+                      int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                      void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state, chunk_states,
+                  true, batch, dim, dstate, seqlen, stream);
+}
+
+int64_t ssm_scan_ckpt_count(int64_t seqlen) { return ckpt_count(seqlen); }
+
+int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                 const void* C, const float* D, const void* z, const float* delta_bias,
+                 uint32_t flags, const float* chunk_states, const void* dout,
+                 const float* dfinal, void* du, void* ddelta, float* dA, float* dB, float* dC,
+                 float* dD, void* dz, float* dbias, float* dh0, int64_t batch, int64_t dim,
+                 int64_t dstate, int64_t seqlen, void* stream) {
+  const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
+  if (flags & ~known) return SSM_ERR_INVALID_ARG;
+  if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return SSM_ERR_INVALID_ARG;
+  const uint32_t io = flags & SSM_IO_MASK;
+  if (io != SSM_IO_F32 && io != SSM_IO_BF16) return SSM_ERR_UNSUPPORTED;
+  if (dstate < 1 || dstate > 64) return SSM_ERR_UNSUPPORTED;
+  const int64_t esz = (io == SSM_IO_BF16) ? 2 : 4;
+
+  int64_t rows, elems, bc, state, a_elems, ck;
+  if (!mul_ok(batch, dim, &rows) || !mul_ok(rows, seqlen, &elems) || !mul_ok(elems, esz, &ck) ||
+      !mul_ok(batch, dstate, &bc) || !mul_ok(bc, seqlen, &bc) || !mul_ok(bc, 4, &ck) ||
+      !mul_ok(rows, dstate, &state) || !mul_ok(state, 4, &ck) || !mul_ok(dim, dstate, &a_elems) ||
+      !mul_ok(state, ckpt_count(seqlen), &ck) || !mul_ok(ck, 4, &ck))
+    return SSM_ERR_UNSUPPORTED;
+  if (rows > kInt32Max || seqlen > kInt32Max || dim > kInt32Max || rows / 64 + 1 > kInt32Max)
+    return SSM_ERR_UNSUPPORTED;
+  if (seqlen * esz > (int64_t(1) << 31) || dstate * seqlen * esz > (int64_t(1) << 31))
+    return SSM_ERR_UNSUPPORTED;
+
+  // required arrays (NULL only when empty)
+  if (elems > 0 && (!u || !delta || !dout || !du || !ddelta)) return SSM_ERR_INVALID_ARG;
+  if (bc > 0 && (!B || !C || !dB || !dC)) return SSM_ERR_INVALID_ARG;
+  if (a_elems > 0 && (!A || !dA)) return SSM_ERR_INVALID_ARG;
+  if (elems > 0 && !chunk_states) return SSM_ERR_INVALID_ARG;
+  if (z && elems > 0 && !dz) return SSM_ERR_INVALID_ARG;
+
+  const uintptr_t ea = static_cast<uintptr_t>(esz);
+  if (!aligned(u, ea) || !aligned(delta, ea) || !aligned(B, ea) || !aligned(C, ea) ||
+      !aligned(dout, ea) || !aligned(du, ea) || !aligned(ddelta, ea) || (z && !aligned(z, ea)) ||
+      (dz && !aligned(dz, ea)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+      (delta_bias && !aligned(delta_bias, 4)) || !aligned(chunk_states, 4) ||
+      (dfinal && !aligned(dfinal, 4)) || !aligned(dA, 4) || !aligned(dB, 4) ||
+      !aligned(dC, 4) || (dD && !aligned(dD, 4)) || (dbias && !aligned(dbias, 4)) ||
+      (dh0 && !aligned(dh0, 4)))
+    return SSM_ERR_MISALIGNED;
+
+  if (rows == 0 && bc == 0 && a_elems == 0) return SSM_OK;
+  if (seqlen == 0) {
+    // Nothing to differentiate through: the state gradient passes straight back.
+    int st = 0;
+    if (a_elems > 0) st = ssm::launch_fill_zero(dA, a_elems, stream);
+    if (st == 0 && D && dD && dim > 0) st = ssm::launch_fill_zero(dD, dim, stream);
+    if (st == 0 && delta_bias && dbias && dim > 0) st = ssm::launch_fill_zero(dbias, dim, stream);
+    if (st == 0 && dh0 && state > 0) {
+      if (dfinal)
+        st = int(hipMemcpyAsync(dh0, dfinal, size_t(state) * 4, hipMemcpyDeviceToDevice,
+                                static_cast<hipStream_t>(stream)));
+      else
+        st = ssm::launch_fill_zero(dh0, state, stream);
+    }
+    return st == 0 ? SSM_OK : SSM_ERR_HIP;
+  }
+  if (rows == 0) {  // no channel: every summed gradient is zero
+    int st = 0;
+    if (bc > 0) st = ssm::launch_fill_zero(dB, bc, stream);
+    if (st == 0 && bc > 0) st = ssm::launch_fill_zero(dC, bc, stream);
+    if (st == 0 && a_elems > 0) st = ssm::launch_fill_zero(dA, a_elems, stream);
+    return st == 0 ? SSM_OK : SSM_ERR_HIP;
+  }
+
+  ssm::BwdArgs a;
+  a.u = u;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.z = z;
+  a.bias = delta_bias;
+  a.ckpt = chunk_states;
+  a.dout = dout;
+  a.dfinal = dfinal;
+  a.du = du;
+  a.ddelta = ddelta;
+  a.dA = dA;
+  a.dB = dB;
+  a.dC = dC;
+  a.dD = D ? dD : nullptr;
+  a.dz = dz;
+  a.dbias = delta_bias ? dbias : nullptr;
+  a.dh0 = dh0;
+  a.batch = batch;
+  a.dim = dim;
+  a.dstate = dstate;
+  a.seqlen = seqlen;
+  a.io = (io == SSM_IO_BF16) ? ssm::Io::BF16 : ssm::Io::F32;
+  a.softplus = (flags & SSM_DELTA_SOFTPLUS) != 0;
+  a.vec_ok = ((seqlen * esz) % 16 == 0) && aligned(u, 16) && aligned(delta, 16) &&
+             aligned(dout, 16) && aligned(du, 16) && aligned(ddelta, 16) && aligned(B, 16) &&
+             aligned(C, 16) && (!z || (aligned(z, 16) && aligned(dz, 16)));
+  return ssm::launch_scan_bwd(a, stream) == 0 ? SSM_OK : SSM_ERR_HIP;
 }
 
 int ssm_scan_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,

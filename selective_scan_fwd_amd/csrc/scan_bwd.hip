@@ -1,0 +1,364 @@
+// Selective-scan backward for gfx950 (CDNA4, wave64).
+//
+// Gradients of L = sum(dout * out) + sum(dfinal * final_state) for the forward of
+// include/ssm_scan.h. The forward saves the state every kCkptInterval steps; the backward
+// restarts from those states and recomputes the scan inside each interval instead of
+// keeping every h_t, which is how p1 (mhpq.cn/news/1077344, section 3.3) describes the
+// backward of a fused scan: only chunk-boundary states are stored, the scan is run again
+// from them, then the gradients are formed.
+//
+// With s_t the step size, a_t = exp(s_t A), c_t = C_t dy_t and g_t = dL/dh_t, the state
+// adjoint runs backwards in time, g_t = c_t + a_{t+1} g_{t+1}. In the pre-multiplied form
+// e_t = a_t g_t it is a linear recurrence read from the right, e_t = a_t e_{t+1} + a_t c_t,
+// so it has the same combine as the forward, (a1,b1) o (a2,b2) = (a2 a1, a2 b1 + b2), with
+// the later step first. A lane folds its steps from the right into one operator, the wave
+// scans those operators from lane 63 down to lane 0, and each lane replays its steps with
+// the adjoint entering from its right, forming per step:
+//   dC_t += dy_t h_t,  dB_t += g_t s_t u_t  (summed over the workgroup's channels in LDS,
+//   then over workgroups with float atomics), du_t += g_t s_t B_t,
+//   ds_t += g_t (A a_t h_{t-1} + B_t u_t), dA += g_t a_t s_t h_{t-1}.
+// The mapping is the forward's: a workgroup owns K channels of one batch row, one
+// wavefront per channel, and lane i owns T consecutive steps of a 64*T-step interval; the
+// intervals are processed last to first, carrying the state adjoint between them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_math.h"
+#include "device_scan.h"
+#include "scan_launch.h"
+
+namespace ssm {
+namespace {
+
+struct BParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const float* ckpt;
+  const void* dout;
+  const float* dfinal;
+  void* du;
+  void* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  void* dz;
+  float* dbias;
+  float* dh0;
+  int dim, dstate, seqlen, dblocks, softplus, n_ckpt;
+};
+
+// Inclusive scan from the right: lane i ends with the composition of the operators of
+// lanes i..63, lane 63 applied first: (a, b) <- (a_i a_j, a_i b_j + b_i), j = i + k.
+__device__ __forceinline__ void wave_scan_from_right(float& a, float& b, int lane) {
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const float aj = __shfl_down(a, k, 64);
+    const float bj = __shfl_down(b, k, 64);
+    if (lane + k < 64) {
+      b = __builtin_fmaf(a, bj, b);
+      a = a * aj;
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+template <typename Elem, int T, int K, bool kVecRows>
+__global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
+  constexpr int kVec = Vec<Elem>::kN;
+  constexpr int kChunk = 64 * T;
+  constexpr int kBlocks = T / kVec;
+  constexpr uint32_t kEsz = sizeof(Elem);
+  constexpr int kPitch = 65;  // LDS row pitch of the dB/dC sums: [step j][lane]
+  static_assert(kChunk == kCkptInterval, "one interval per saved state");
+  static_assert(T % kVec == 0, "whole 16-byte words per lane");
+
+  __shared__ float acc[2][2][T * kPitch];  // [state parity][dB / dC][j * kPitch + lane]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x / p.dblocks;
+  const int d = (blockIdx.x - b * p.dblocks) * K + wave;
+  const bool active = d < p.dim;
+  const int N = p.dstate, L = p.seqlen;
+  const int n_chunks = (L + kChunk - 1) / kChunk;
+  const int64_t row = int64_t(b) * p.dim + (active ? d : 0);
+
+  const uint32_t row_bytes = active ? uint32_t(L) * kEsz : 0u;
+  const Buf u_buf(static_cast<const Elem*>(p.u) + row * L, row_bytes);
+  const Buf dl_buf(static_cast<const Elem*>(p.delta) + row * L, row_bytes);
+  const Buf do_buf(static_cast<const Elem*>(p.dout) + row * L, row_bytes);
+  const Buf z_buf(static_cast<const Elem*>(p.z ? p.z : p.u) + row * L, p.z ? row_bytes : 0u);
+  const Buf du_buf(static_cast<Elem*>(p.du) + row * L, row_bytes);
+  const Buf dd_buf(static_cast<Elem*>(p.ddelta) + row * L, row_bytes);
+  const Buf dz_buf(static_cast<Elem*>(p.z ? p.dz : p.du) + row * L, p.z ? row_bytes : 0u);
+  const uint32_t bc_elems = uint32_t(N) * uint32_t(L);
+  const Buf B_buf(static_cast<const Elem*>(p.B) + int64_t(b) * N * L, bc_elems * kEsz);
+  const Buf C_buf(static_cast<const Elem*>(p.C) + int64_t(b) * N * L, bc_elems * kEsz);
+
+  // Per-state values live in lane n of these registers.
+  float A_l = 0.0f, gc_l = 0.0f, dA_l = 0.0f, Dd = 0.0f, bias_d = 0.0f;
+  if (active) {
+    Dd = p.D ? p.D[d] : 0.0f;
+    bias_d = p.bias ? p.bias[d] : 0.0f;
+    if (lane < N) {
+      A_l = p.A[int64_t(d) * N + lane];
+      if (p.dfinal) gc_l = p.dfinal[row * N + lane];  // e_{L-1} = dfinal
+    }
+  }
+  const float a2_l = A_l * kLog2e;
+  float dD_acc = 0.0f, db_acc = 0.0f;
+
+  {
+    float* flat = &acc[0][0][0];
+    for (int i = tid; i < 2 * 2 * T * kPitch; i += 64 * K) flat[i] = 0.0f;
+  }
+  __syncthreads();
+
+  // B or C words of state n for this lane's steps (zeros past the end of the sequence).
+  auto load_bc = [&](const Buf& buf, int n, int tb, float (&v)[T]) {
+#pragma unroll
+    for (int q = 0; q < kBlocks; ++q) {
+      const int t0 = tb + q * kVec;
+      const uint32_t e = (t0 < L) ? uint32_t(n) * uint32_t(L) + uint32_t(t0) : bc_elems;
+      widen_raw16<Elem>(load_word<Elem, kVecRows>(buf, e), &v[q * kVec]);
+    }
+  };
+
+  int it = 0;  // states processed so far: selects the LDS buffer
+  for (int c = n_chunks - 1; c >= 0; --c) {
+    const int tb = c * kChunk + lane * T;
+    float uv[T], sv[T], xv[T], dyv[T], gdu[T], gds[T];
+    float sdt = 0.0f;
+    {
+      float dov[T], zv[T];
+#pragma unroll
+      for (int q = 0; q < kBlocks; ++q) {
+        const uint32_t e = uint32_t(tb + q * kVec);
+        widen_raw16<Elem>(load_word<Elem, kVecRows>(u_buf, e), &uv[q * kVec]);
+        widen_raw16<Elem>(load_word<Elem, kVecRows>(dl_buf, e), &xv[q * kVec]);
+        widen_raw16<Elem>(load_word<Elem, kVecRows>(do_buf, e), &dov[q * kVec]);
+        widen_raw16<Elem>(load_word<Elem, kVecRows>(z_buf, e), &zv[q * kVec]);
+      }
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        xv[j] += bias_d;
+        float s = p.softplus ? softplus_f(xv[j]) : xv[j];
+        if (tb + j >= L) s = uv[j] = dov[j] = 0.0f;  // past the end: identity steps
+        sv[j] = s;
+        sdt += s;
+        dyv[j] = dov[j];
+      }
+      const float hc_l = (active && lane < N) ? p.ckpt[(row * p.n_ckpt + c) * N + lane] : 0.0f;
+
+      if (p.z) {
+        // The gate needs y (before the gate): a forward pass over every state.
+        float y[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) y[j] = Dd * uv[j];
+        if (active) {
+          for (int n = 0; n < N; ++n) {
+            const float a2 = readlane(a2_l, n), hc = readlane(hc_l, n);
+            float Bv[T], Cv[T], dA[T], dBu[T];
+            load_bc(B_buf, n, tb, Bv);
+            load_bc(C_buf, n, tb, Cv);
+            float bseg = (lane == 0) ? hc : 0.0f;
+#pragma unroll
+            for (int j = 0; j < T; ++j) {
+              dA[j] = exp2_hw(sv[j] * a2);
+              dBu[j] = (sv[j] * uv[j]) * Bv[j];
+              bseg = __builtin_fmaf(dA[j], bseg, dBu[j]);
+            }
+            float aseg = exp2_hw(sdt * a2);
+            wave_scan_inclusive(aseg, bseg);
+            float h = shift_up_one(bseg, hc);
+#pragma unroll
+            for (int j = 0; j < T; ++j) {
+              h = __builtin_fmaf(dA[j], h, dBu[j]);
+              y[j] = __builtin_fmaf(Cv[j], h, y[j]);
+            }
+          }
+        }
+        float dzv[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const float sg = sigmoid_f(zv[j]);
+          dzv[j] = dov[j] * y[j] * sg * __builtin_fmaf(zv[j], 1.0f - sg, 1.0f);
+          dyv[j] = dov[j] * zv[j] * sg;
+        }
+        store_lane_block<Elem, kVecRows, T>(dz_buf, uint32_t(tb), dzv);
+      }
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        dD_acc = __builtin_fmaf(dyv[j], uv[j], dD_acc);
+        gdu[j] = Dd * dyv[j];
+        gds[j] = 0.0f;
+      }
+
+      for (int n = 0; n < N; ++n) {
+        const int par = it & 1;
+        if (active) {
+          const float a2 = readlane(a2_l, n), An = readlane(A_l, n);
+          const float hc = readlane(hc_l, n), G = readlane(gc_l, n);
+          float Bv[T], Cv[T], dA[T], h[T];
+          load_bc(B_buf, n, tb, Bv);
+          load_bc(C_buf, n, tb, Cv);
+          // forward again from the saved state: h_t for this lane's steps
+          float bseg = (lane == 0) ? hc : 0.0f;
+#pragma unroll
+          for (int j = 0; j < T; ++j) {
+            dA[j] = exp2_hw(sv[j] * a2);
+            bseg = __builtin_fmaf(dA[j], bseg, (sv[j] * uv[j]) * Bv[j]);
+          }
+          const float alpha = exp2_hw(sdt * a2);  // product of the lane's a_t
+          float aseg = alpha;
+          wave_scan_inclusive(aseg, bseg);
+          const float hin = shift_up_one(bseg, hc);  // state entering the lane's steps
+          {
+            float hh = hin;
+#pragma unroll
+            for (int j = 0; j < T; ++j) {
+              hh = __builtin_fmaf(dA[j], hh, (sv[j] * uv[j]) * Bv[j]);
+              h[j] = hh;
+            }
+          }
+          // adjoint: fold the lane's steps from the right, scan from lane 63 down
+          float beta = 0.0f;
+#pragma unroll
+          for (int j = T - 1; j >= 0; --j) beta = dA[j] * __builtin_fmaf(Cv[j], dyv[j], beta);
+          float ra = alpha, rb = beta;
+          wave_scan_from_right(ra, rb, lane);
+          const float an = __shfl_down(ra, 1, 64), bn = __shfl_down(rb, 1, 64);
+          float v = (lane == 63) ? G : __builtin_fmaf(an, G, bn);  // e entering from the right
+          const float G_next = __builtin_fmaf(readlane(ra, 0), G, readlane(rb, 0));
+          gc_l = (lane == n) ? G_next : gc_l;
+          float dAn = 0.0f;
+#pragma unroll
+          for (int j = T - 1; j >= 0; --j) {
+            const float g = __builtin_fmaf(Cv[j], dyv[j], v);  // g_t = C_t dy_t + e_{t+1}
+            const float hp = (j > 0) ? h[j - 1] : hin;
+            const float t1 = dA[j] * hp;
+            atomicAdd(&acc[par][0][j * kPitch + lane], g * (sv[j] * uv[j]));  // dB
+            atomicAdd(&acc[par][1][j * kPitch + lane], dyv[j] * h[j]);        // dC
+            gdu[j] = __builtin_fmaf(g, sv[j] * Bv[j], gdu[j]);
+            gds[j] = __builtin_fmaf(g, __builtin_fmaf(An, t1, Bv[j] * uv[j]), gds[j]);
+            dAn = __builtin_fmaf(g * t1, sv[j], dAn);
+            v = dA[j] * g;  // e_t = a_t g_t
+          }
+          dAn = wave_sum(dAn);
+          dA_l = (lane == n) ? dA_l + dAn : dA_l;
+        }
+        __syncthreads();  // every channel's share of state n is in acc[par]
+        // Add the workgroup's sums for state n into dB and dC, one step per thread, and
+        // clear the buffer. It is written again two states later, after the next barrier,
+        // which no thread passes before finishing this loop.
+        for (int i = tid; i < kChunk; i += 64 * K) {
+          const int ln = i / T, j = i - ln * T;
+          const int t = c * kChunk + i;
+          float* sb = &acc[par][0][j * kPitch + ln];
+          float* sc = &acc[par][1][j * kPitch + ln];
+          const float vb = *sb, vc = *sc;
+          *sb = 0.0f;
+          *sc = 0.0f;
+          if (t < L) {
+            const int64_t o = (int64_t(b) * N + n) * L + t;
+            unsafeAtomicAdd(&p.dB[o], vb);
+            unsafeAtomicAdd(&p.dC[o], vc);
+          }
+        }
+        ++it;
+      }
+    }
+    float dd[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const float x = xv[j];
+      dd[j] = p.softplus ? gds[j] * sigmoid_f(x) : gds[j];
+      if (tb + j < L) db_acc += dd[j];
+    }
+    store_lane_block<Elem, kVecRows, T>(du_buf, uint32_t(tb), gdu);
+    store_lane_block<Elem, kVecRows, T>(dd_buf, uint32_t(tb), dd);
+  }
+
+  if (active) {
+    if (lane < N) {
+      if (p.dh0) p.dh0[row * N + lane] = gc_l;  // e_{-1} = a_0 g_0
+      unsafeAtomicAdd(&p.dA[int64_t(d) * N + lane], dA_l);
+    }
+    const float sD = wave_sum(dD_acc), sb = wave_sum(db_acc);
+    if (lane == 0) {
+      if (p.dD) unsafeAtomicAdd(&p.dD[d], sD);
+      if (p.dbias) unsafeAtomicAdd(&p.dbias[d], sb);
+    }
+  }
+}
+
+template <typename Elem, int T, int K>
+int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
+  BParams p;
+  p.u = a.u;
+  p.delta = a.delta;
+  p.A = a.A;
+  p.B = a.B;
+  p.C = a.C;
+  p.D = a.D;
+  p.z = a.z;
+  p.bias = a.bias;
+  p.ckpt = a.ckpt;
+  p.dout = a.dout;
+  p.dfinal = a.dfinal;
+  p.du = a.du;
+  p.ddelta = a.ddelta;
+  p.dA = a.dA;
+  p.dB = a.dB;
+  p.dC = a.dC;
+  p.dD = a.dD;
+  p.dz = a.dz;
+  p.dbias = a.dbias;
+  p.dh0 = a.dh0;
+  p.dim = int(a.dim);
+  p.dstate = int(a.dstate);
+  p.seqlen = int(a.seqlen);
+  p.dblocks = int((a.dim + K - 1) / K);
+  p.softplus = a.softplus ? 1 : 0;
+  p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
+  const int64_t blocks = a.batch * p.dblocks;
+  if (a.vec_ok)
+    hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, true>), dim3(unsigned(blocks)), dim3(64 * K),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, false>), dim3(unsigned(blocks)),
+                       dim3(64 * K), 0, s, p);
+  return int(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_scan_bwd(const BwdArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The channel- and batch-summed gradients are accumulated with atomics.
+  int st = launch_fill_zero(a.dA, a.dim * a.dstate, stream);
+  if (st == 0) st = launch_fill_zero(a.dB, a.batch * a.dstate * a.seqlen, stream);
+  if (st == 0) st = launch_fill_zero(a.dC, a.batch * a.dstate * a.seqlen, stream);
+  if (st == 0 && a.dD) st = launch_fill_zero(a.dD, a.dim, stream);
+  if (st == 0 && a.dbias) st = launch_fill_zero(a.dbias, a.dim, stream);
+  if (st != 0) return st;
+  if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, 8>(a, s);
+  return launch_bwd_typed<float, 8, 8>(a, s);
+}
+
+}  // namespace ssm

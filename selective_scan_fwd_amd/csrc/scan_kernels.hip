@@ -42,184 +42,11 @@
 #include <stdint.h>
 
 #include "device_math.h"
+#include "device_scan.h"
 #include "scan_launch.h"
 
 namespace ssm {
 namespace {
-
-__device__ __forceinline__ float readlane(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// Elements per 16-byte access.
-template <typename Elem>
-struct Vec;
-template <>
-struct Vec<float> {
-  static constexpr int kN = 4;
-};
-template <>
-struct Vec<uint16_t> {
-  static constexpr int kN = 8;
-};
-
-template <typename Elem>
-__device__ __forceinline__ void widen_raw16(uint4 w, float* v);
-template <>
-__device__ __forceinline__ void widen_raw16<float>(uint4 w, float* v) {
-  v[0] = __uint_as_float(w.x);
-  v[1] = __uint_as_float(w.y);
-  v[2] = __uint_as_float(w.z);
-  v[3] = __uint_as_float(w.w);
-}
-template <>
-__device__ __forceinline__ void widen_raw16<uint16_t>(uint4 w, float* v) {
-  v[0] = bf16_lo(w.x);
-  v[1] = bf16_hi(w.x);
-  v[2] = bf16_lo(w.y);
-  v[3] = bf16_hi(w.y);
-  v[4] = bf16_lo(w.z);
-  v[5] = bf16_hi(w.z);
-  v[6] = bf16_lo(w.w);
-  v[7] = bf16_hi(w.w);
-}
-
-// ---------------------------------------------------------------- wave64 combine scan
-
-// Inclusive scan of the operators (a, b) across the 64 lanes of a wavefront, lane 0
-// earliest, under (a1,b1) o (a2,b2) = (a2 a1, a2 b1 + b2).
-//
-// Each Hillis-Steele step is two DPP instructions reading the operator of the lane the
-// control names (earlier in time):
-//   v_fmac_f32_dpp b, b, a   ->  b_i = b_j * a_i + b_i      (uses a_i before its update)
-//   v_mul_f32_dpp  a, a, a   ->  a_i = a_j * a_i
-// Without bound_ctrl, a lane whose source is outside its row, or whose row the row_mask
-// excludes, is not written: it keeps its operator, i.e. combines with the identity (1, 0).
-// Controls: row_shr:1/2/4/8 inside 16-lane rows; row_bcast:15 (lane 15 of a row into the
-// next row; written to rows 1 and 3 by row_mask 0xa); row_bcast:31 (lane 31 into rows 2
-// and 3, row_mask 0xc). The final a is not needed by the caller, so the last step updates
-// b only.
-//
-// gfx950 needs two wait states between a VALU write of a VGPR and a DPP read of it: the
-// block starts with s_nop 1 (its inputs were just written) and every step is followed by
-// s_nop 0, so each DPP read is at least two instructions after the write it depends on.
-__device__ __forceinline__ void wave_scan_inclusive(float& a, float& b) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 0\n\t"
-      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 0\n\t"
-      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 0\n\t"
-      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 0\n\t"
-      "v_fmac_f32_dpp %1, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
-      "s_nop 1\n\t"
-      "v_fmac_f32_dpp %1, %1, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
-      "s_nop 1"
-      : "+v"(a), "+v"(b));
-}
-
-// Lane i receives lane i-1's value; lane 0 receives `first` (DPP wave_shr:1).
-__device__ __forceinline__ float shift_up_one(float v, float first) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(v),
-                                                    0x138, 0xf, 0xf, false));
-}
-
-// ---------------------------------------------------------------- buffer access
-
-// Raw buffer resources (base, byte length): an access at or past the length reads 0 and a
-// store there is dropped by the hardware range check, so tails, inactive waves and the
-// "next chunk" past the end of the sequence need no branches. Branch-free loads also let
-// the compiler count outstanding loads exactly (vmcnt completes in order), which is what
-// keeps a prefetch in flight across later waits.
-constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) dword access
-
-struct Buf {
-  __amdgpu_buffer_rsrc_t r;
-  __device__ Buf(const void* base, uint32_t bytes)
-      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
-                                            kRsrcWord3)) {}
-  __device__ uint4 load16(uint32_t off) const {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  }
-  __device__ uint32_t load4(uint32_t off) const {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-  }
-  __device__ uint32_t load2(uint32_t off) const {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  }
-  __device__ void store16(uint4 v, uint32_t off) const {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
-  }
-  __device__ void store4(uint32_t v, uint32_t off) const {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
-  }
-  __device__ void store2(uint16_t v, uint32_t off) const {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
-  }
-};
-
-// One 16-byte word of storage elements starting at element e (byte offset e*sizeof). With
-// kVecRows every such word is 16-byte aligned and lies wholly inside or outside the row;
-// otherwise it is gathered element by element.
-template <typename Elem, bool kVecRows>
-__device__ __forceinline__ uint4 load_word(const Buf& b, uint32_t e) {
-  if constexpr (kVecRows) {
-    return b.load16(e * uint32_t(sizeof(Elem)));
-  } else if constexpr (sizeof(Elem) == 4) {
-    return make_uint4(b.load4(4 * e), b.load4(4 * e + 4), b.load4(4 * e + 8), b.load4(4 * e + 12));
-  } else {
-    uint32_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = b.load2(2 * e + 4 * k) | (b.load2(2 * e + 4 * k + 2) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-template <typename Elem, bool kVecRows, int T>
-__device__ __forceinline__ void store_lane_block(const Buf& b, uint32_t e0, const float (&v)[T]) {
-  if constexpr (sizeof(Elem) == 4) {
-#pragma unroll
-    for (int q = 0; q < T / 4; ++q) {
-      const uint4 w = make_uint4(__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
-                                 __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3]));
-      if constexpr (kVecRows) {
-        b.store16(w, 4 * (e0 + 4 * q));
-      } else {
-        b.store4(w.x, 4 * (e0 + 4 * q));
-        b.store4(w.y, 4 * (e0 + 4 * q + 1));
-        b.store4(w.z, 4 * (e0 + 4 * q + 2));
-        b.store4(w.w, 4 * (e0 + 4 * q + 3));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < T / 8; ++q) {
-      const uint4 w = make_uint4(pack_bf16x2(v[8 * q + 0], v[8 * q + 1]),
-                                 pack_bf16x2(v[8 * q + 2], v[8 * q + 3]),
-                                 pack_bf16x2(v[8 * q + 4], v[8 * q + 5]),
-                                 pack_bf16x2(v[8 * q + 6], v[8 * q + 7]));
-      if constexpr (kVecRows) {
-        b.store16(w, 2 * (e0 + 8 * q));
-      } else {
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          b.store2(uint16_t(ws[k]), 2 * (e0 + 8 * q + 2 * k));
-          b.store2(uint16_t(ws[k] >> 16), 2 * (e0 + 8 * q + 2 * k + 1));
-        }
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------- forward kernel
 
@@ -234,9 +61,11 @@ struct KParams {
   const float* bias;
   void* out;
   float* final_state;
+  float* ckpt;  // nullable: states at every kCkptInterval steps, [rows, n_ckpt, dstate]
   int dim, dstate, seqlen;
   int dblocks;  // ceil(dim / K)
   int softplus, initial_state;
+  int n_ckpt;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -250,6 +79,7 @@ template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs>
 __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   constexpr int kVec = Vec<Elem>::kN;          // elements per 16-byte word
   constexpr int kChunk = 64 * T;               // steps per chunk
+  static_assert(kChunk == 2 * kCkptInterval, "checkpoints sit at chunk starts and halves");
   constexpr int kQuads = T / 4;                // float4 LDS words per lane per state
   constexpr int kWordsPerState = kChunk / kVec;      // 16-byte words per state per chunk
   constexpr int kArrayWords = G * kWordsPerState;    // words per array (B or C) per stage
@@ -286,7 +116,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   const Buf B_buf(static_cast<const Elem*>(p.B) + int64_t(b) * N * L, bc_elems * kEsz);
   const Buf C_buf(static_cast<const Elem*>(p.C) + int64_t(b) * N * L, bc_elems * kEsz);
 
-  float Dd = 0.0f, bias_d = 0.0f, a2_lane = 0.0f, hc_lane = 0.0f;
+  float Dd = 0.0f, bias_d = 0.0f, a2_lane = 0.0f, hc_lane = 0.0f, mid_lane = 0.0f;
   if (active) {
     Dd = p.D ? p.D[d] : 0.0f;
     bias_d = p.bias ? p.bias[d] : 0.0f;
@@ -421,6 +251,12 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
         const float carry_out = readlane(bseg, 63);
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
         hc_lane = (lane == n) ? carry_out : hc_lane;
+        if (p.ckpt) {
+          // the state after the first half of the chunk: the last step of the lane before
+          // the one whose segment starts at kCkptInterval
+          const float mid = readlane(bseg, kCkptInterval / T - 1);
+          mid_lane = (lane == n) ? mid : mid_lane;
+        }
 #pragma unroll
         for (int q = 0; q < kQuads; ++q) {
           const float cc[4] = {cq[q].x, cq[q].y, cq[q].z, cq[q].w};
@@ -449,6 +285,8 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   for (int c = 0; c < n_chunks; ++c) {
     const int tb = c * kChunk + lane * T;
     sdt = 0.0f;
+    if (p.ckpt && active && lane < N)  // the state entering the chunk
+      p.ckpt[(row * p.n_ckpt + 2 * c) * N + lane] = hc_lane;
     {
       const bool tail = (c + 1) * kChunk > L;
 #pragma unroll
@@ -520,6 +358,8 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
       }
     }
     store_lane_block<Elem, kVecRows, T>(out_buf, uint32_t(tb), y);
+    if (p.ckpt && active && lane < N && 2 * c + 1 < p.n_ckpt)
+      p.ckpt[(row * p.n_ckpt + 2 * c + 1) * N + lane] = mid_lane;
   }
 
   if (active && p.final_state && lane < N) p.final_state[row * N + lane] = hc_lane;
@@ -562,6 +402,8 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
   p.dblocks = int((a.dim + K - 1) / K);
   p.softplus = a.softplus ? 1 : 0;
   p.initial_state = a.initial_state ? 1 : 0;
+  p.ckpt = a.ckpt;
+  p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
   const int64_t blocks = a.batch * p.dblocks;
   if (a.vec_ok)
     hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, true, kDma>), dim3(unsigned(blocks)),

@@ -24,7 +24,12 @@ struct FwdArgs {
   bool softplus;
   bool initial_state;
   bool vec_ok;             // every row of every streamed array starts 16-byte aligned
+  float* ckpt = nullptr;   // nullable: states every kCkptInterval steps [rows, n_ckpt, dstate]
 };
+
+// Spacing of the saved states that the backward pass restarts from (the state entering
+// steps 0, kCkptInterval, 2 kCkptInterval, ...). Equals SSM_CKPT_INTERVAL in ssm_scan.h.
+constexpr int kCkptInterval = 512;
 
 // Sequences of at most this many steps take the short-sequence kernel (one lane per
 // channel and state, stepping through time); longer ones the chunked scan kernel.
@@ -32,12 +37,43 @@ struct FwdArgs {
 #define SSM_SHORT_MAX_L 32
 #endif
 constexpr int64_t kShortMaxSeqlen = SSM_SHORT_MAX_L;
+static_assert(SSM_SHORT_MAX_L < 512, "the short kernel saves a single state");
 
 // Each returns a hipError_t value (0 on success).
 int launch_scan_fwd(const FwdArgs& a, void* stream);    // dispatches on seqlen
 int launch_scan_short(const FwdArgs& a, void* stream);  // short-sequence kernel
 int launch_scan_chunked(const FwdArgs& a, void* stream);  // chunked scan kernel
 int launch_fill_zero(float* p, int64_t count, void* stream);
+
+// Everything a backward launch needs, already validated by the C-ABI layer.
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // nullable
+  const void* z;         // nullable
+  const float* bias;     // nullable
+  const float* ckpt;     // [rows, n_ckpt, dstate] from the forward
+  const void* dout;
+  const float* dfinal;   // nullable
+  void* du;
+  void* ddelta;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;             // nullable
+  void* dz;              // required when z is given
+  float* dbias;          // nullable
+  float* dh0;            // nullable
+  int64_t batch, dim, dstate, seqlen;
+  Io io;
+  bool softplus;
+  bool vec_ok;
+};
+
+int launch_scan_bwd(const BwdArgs& a, void* stream);
 int launch_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
                               int64_t groups, void* stream);
 

@@ -34,6 +34,7 @@ struct ShortParams {
   const float* bias;
   void* out;
   float* final_state;
+  float* ckpt;   // nullable: [rows, 1, dstate], the state entering step 0
   int64_t rows;  // batch * dim
   int dim, dstate, seqlen;
   int n2_log2;
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void scan_short_kernel(ShortParams p) {
   const float Dd = (row_ok && p.D) ? p.D[d] : 0.0f;
   const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
   float h = (lane_ok && p.initial_state) ? p.final_state[rr * N + n] : 0.0f;
+  if (lane_ok && p.ckpt) p.ckpt[rr * N + n] = h;  // seqlen <= 32: one saved state
   const int64_t bc0 = (b * N + (lane_ok ? n : 0)) * L;  // B[b, n, 0], C[b, n, 0]
   const int64_t x0 = rr * L;                           // u, delta, z, out [b, d, 0]
 
@@ -121,6 +123,7 @@ int launch_scan_short(const FwdArgs& a, void* stream) {
   p.bias = a.bias;
   p.out = a.out;
   p.final_state = a.final_state;
+  p.ckpt = a.ckpt;
   p.rows = a.batch * a.dim;
   p.dim = int(a.dim);
   p.dstate = int(a.dstate);

@@ -1,0 +1,167 @@
+"""GPU backward pass (through the C ABI) against the float64 backward oracle, and the
+forward's saved states against the forward oracle.
+
+Bar, per tensor (the metric of ssm_workloads.compare, max |g - r| / (|r| + rms(r))):
+  * du, ddelta, dz: 1e-4 with float32 storage, 2e-2 with bfloat16 storage (one rounding
+    to bf16 on store, as for out);
+  * dA, dB, dC, dD, dbias, dh0 and the saved states (always float32): 1e-4, which leaves
+    about two orders of magnitude over the float32 rounding of sums of up to ~1e4 terms.
+The channel- and batch-summed gradients use float atomics, so only du, ddelta, dz and dh0
+are compared bit for bit between runs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import selective_scan_fwd_amd as ssm
+from gpu_util import announce, dev, host, torch
+from ssm_workloads import RTOL, WORKLOADS, f32_to_bf16_bits, make_inputs, parity, widen
+
+pytestmark = pytest.mark.gpu
+
+RTOL_F32_OUT = 1e-4
+PER_ELEMENT = ("du", "ddelta", "dz")
+
+
+def setup(w, softplus=True, use_D=True, use_z=True, use_bias=True, dfinal=True, seed=0):
+    inp = make_inputs(w)
+    if not use_z:
+        inp["z"] = None
+    if not use_D:
+        inp["D"] = None
+    if not use_bias:
+        inp["delta_bias"] = None
+    if not softplus:
+        raw = widen(inp["delta"], w.io)
+        pos = (np.abs(raw) * 0.05 + 1e-3).astype(np.float32)
+        inp["delta"] = pos if w.io == "f32" else f32_to_bf16_bits(pos)
+        if inp["delta_bias"] is not None:  # delta + bias is the step size: keep it positive
+            inp["delta_bias"] = np.abs(inp["delta_bias"]) * 0.01
+    rng = np.random.default_rng(seed + 991)
+    dout = rng.standard_normal(inp["u"].shape).astype(np.float32)
+    if w.io == "bf16":
+        dout = f32_to_bf16_bits(dout)
+    dfin = rng.standard_normal((w.batch, w.dim, w.dstate)).astype(np.float32) if dfinal else None
+    return inp, dout, dfin
+
+
+def run_gpu(inp, dout, dfin, softplus):
+    io = inp["io"]
+    g = {k: dev(inp[k], io) for k in ("u", "delta", "B", "C", "z")}
+    f = {k: dev(inp[k], "f32") for k in ("A", "D", "delta_bias", "h0")}
+    out, fin, states = ssm.scan_train(g["u"], g["delta"], f["A"], g["B"], g["C"], D=f["D"],
+                                      z=g["z"], delta_bias=f["delta_bias"],
+                                      delta_softplus=softplus, h0=f["h0"])
+    grads = ssm.scan_backward(g["u"], g["delta"], f["A"], g["B"], g["C"], states,
+                              dev(dout, io), D=f["D"], z=g["z"], delta_bias=f["delta_bias"],
+                              delta_softplus=softplus,
+                              dfinal=None if dfin is None else dev(dfin, "f32"))
+    torch().cuda.synchronize()
+    res = {k: (None if v is None else host(v)) for k, v in grads.items()}
+    return host(out), host(fin), host(states), res
+
+
+def run_oracle(inp, dout, dfin, softplus):
+    io = inp["io"]
+    return oracle.scan_bwd_ref(
+        widen(inp["u"], io), widen(inp["delta"], io), inp["A"], widen(inp["B"], io),
+        widen(inp["C"], io), inp["D"], None if inp["z"] is None else widen(inp["z"], io),
+        inp["delta_bias"], softplus, inp["h0"], widen(dout, io),
+        None if dfin is None else dfin.astype(np.float64))
+
+
+def compare(io, got, ref, label):
+    for k, r in ref.items():
+        if r is None:
+            assert got.get(k) is None, f"{label}: {k} should be absent"
+            continue
+        rtol = RTOL[io] if k in PER_ELEMENT else RTOL_F32_OUT
+        rep = parity(got[k], r, rtol)
+        print(f"[grad] {label} {k}: {rep}", flush=True)
+        assert rep.ok, f"{label} {k}: {rep}"
+
+
+SHAPES = [
+    # (batch, dim, dstate, seqlen): one step, a ragged tail, one and several 512-step
+    # intervals, ragged channel counts, 1 to 64 states
+    (2, 5, 16, 1), (1, 7, 3, 7), (2, 9, 16, 100), (1, 6, 16, 512), (1, 6, 16, 513),
+    (2, 5, 4, 1500), (1, 3, 64, 700), (1, 10, 1, 300), (1, 4, 17, 2049),
+]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}d{}N{}L{}".format(*s))
+def test_backward_shapes(shape, io):
+    b, d, n, L = shape
+    w = WORKLOADS["tiny"].with_(batch=b, dim=d, dstate=n, seqlen=L, io=io, gate=True,
+                                initial_state=True, a_kind="scaled", seed=600 + L + n)
+    announce(w.describe() + " backward")
+    inp, dout, dfin = setup(w, seed=L)
+    *_, got = run_gpu(inp, dout, dfin, True)
+    compare(io, got, run_oracle(inp, dout, dfin, True), w.describe())
+
+
+@pytest.mark.parametrize("variant", ["no_D", "no_z", "no_bias", "no_softplus", "no_dfinal",
+                                     "bare"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_optional_inputs(variant, io):
+    w = WORKLOADS["tiny"].with_(batch=2, dim=12, dstate=16, seqlen=600, io=io, gate=True,
+                                initial_state=variant not in ("bare",), seed=61)
+    announce(f"{w.describe()} backward {variant}")
+    bare = variant == "bare"
+    kw = dict(softplus=variant not in ("no_softplus", "bare"),
+              use_D=variant not in ("no_D", "bare"), use_z=variant not in ("no_z", "bare"),
+              use_bias=variant not in ("no_bias", "bare"),
+              dfinal=variant not in ("no_dfinal", "bare"))
+    inp, dout, dfin = setup(w, seed=62, **kw)
+    *_, got = run_gpu(inp, dout, dfin, kw["softplus"])
+    compare(io, got, run_oracle(inp, dout, dfin, kw["softplus"]), f"{w.describe()} {variant}")
+    if bare:
+        assert got["dD"] is None and got["dz"] is None and got["dbias"] is None
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_saved_states_and_forward_unchanged(io):
+    w = WORKLOADS["tiny"].with_(batch=2, dim=6, dstate=16, seqlen=1700, io=io, gate=True,
+                                initial_state=True, seed=63)
+    announce(w.describe() + " saved states")
+    inp, dout, dfin = setup(w, seed=63)
+    out, fin, states, _ = run_gpu(inp, dout, dfin, True)
+    # the training forward writes the same out and final state as the plain forward
+    from gpu_util import run_hip
+    o2, f2 = run_hip(inp)
+    assert np.array_equal(out, o2) and np.array_equal(fin, f2)
+    # entry k is the state entering step 512 k
+    io_ = inp["io"]
+    for k in range(states.shape[2]):
+        t = 512 * k
+        if t == 0:
+            ref = inp["h0"].astype(np.float64)
+        else:
+            _, ref = oracle.scan_ref(
+                widen(inp["u"][..., :t], io_), widen(inp["delta"][..., :t], io_), inp["A"],
+                widen(inp["B"][..., :t], io_), widen(inp["C"][..., :t], io_), inp["D"],
+                widen(inp["z"][..., :t], io_), inp["delta_bias"], True, inp["h0"])
+        rep = parity(states[:, :, k], ref, RTOL_F32_OUT)
+        assert rep.ok, f"state {k}: {rep}"
+
+
+def test_backward_per_element_outputs_are_deterministic():
+    w = WORKLOADS["tiny"].with_(batch=2, dim=16, dstate=16, seqlen=1100, io="bf16", gate=True,
+                                initial_state=True, seed=64)
+    announce(w.describe() + " determinism")
+    inp, dout, dfin = setup(w, seed=64)
+    *_, g1 = run_gpu(inp, dout, dfin, True)
+    *_, g2 = run_gpu(inp, dout, dfin, True)
+    for k in ("du", "ddelta", "dz", "dh0"):
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+def test_backward_layer_workload_full():
+    """The benchmark's layer shape (b4 d2048 N16 L2048 bf16, gated): every gradient
+    against the oracle, whole tensors."""
+    w = WORKLOADS["layer"]
+    announce(w.describe() + " backward")
+    inp, dout, dfin = setup(w, seed=65)
+    *_, got = run_gpu(inp, dout, dfin, True)
+    compare(w.io, got, run_oracle(inp, dout, dfin, True), w.describe())
