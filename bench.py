@@ -39,31 +39,38 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
 # slot as one FMA (2 flop), an update is 16 flop-equivalents against the 157.3 peak.
 ALU_PEAK_TFLOPS = 157.3
 FLOP_EQ_PER_UPDATE = 16
+# The backward's minimal work per update (the sequential adjoint): recompute the state
+# (s*A, exp, (s*u)*B, fma: 6 slots), g = C dy + e (1), dC += dy h (1), dB += g s u (1),
+# du += g s B (2), a h_prev (1), ds += g (A a h_prev + B u) (3), dA += g a h_prev s (2),
+# e = a g (1): 18 issue slots = 36 flop-equivalents.
+BWD_FLOP_EQ_PER_UPDATE = 36
 INFINITY_CACHE_BYTES = 256 << 20
-KERNEL_SOURCES = ["selective_scan_fwd_amd/csrc/scan_kernels.hip",
-                  "selective_scan_fwd_amd/csrc/scan_short.hip",
-                  "selective_scan_fwd_amd/csrc/device_math.h",
-                  "selective_scan_fwd_amd/csrc/scan_launch.h"]
+_CSRC = "selective_scan_fwd_amd/csrc/"
+_SHARED = [_CSRC + "device_math.h", _CSRC + "device_scan.h", _CSRC + "scan_launch.h"]
+KERNEL_SOURCES = {"fwd": [_CSRC + "scan_kernels.hip", _CSRC + "scan_short.hip"] + _SHARED,
+                  "bwd": [_CSRC + "scan_bwd.hip"] + _SHARED}
 SHORT_MAX_SEQLEN = 32   # sequences up to this length take the short-sequence kernel
 
 
-def kernel_hash() -> str:
+def kernel_hash(direction: str = "fwd") -> str:
+    """sha256 (first 16 hex) of the sources of one direction's kernels: a committed traffic
+    record counts only while it matches."""
     h = hashlib.sha256()
-    for s in KERNEL_SOURCES:
+    for s in KERNEL_SOURCES[direction]:
         with open(os.path.join(ROOT, s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, direction: str = "fwd"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
     the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"scan_fwd_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"scan_{direction}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash(direction):
         return None
     return rec.get("bytes_per_launch")
 
@@ -149,6 +156,146 @@ def copy_probe(torch, steps: int, warmup: int) -> int:
     return 0
 
 
+def timed_launches(launch, steps, warmup, stream, torch):
+    """W untimed calls, then K calls between two synchronisations, each between its own
+    pair of HIP events on the launch stream. Returns (wall seconds, per-call ms array)."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
+    """The backward pass: ssm_scan_bwd on resident inputs, dout, dfinal and the saved
+    states of a training forward (run once per buffer set, untimed)."""
+    io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
+    flags = (ssm.SSM_IO_BF16 if w.io == "bf16" else ssm.SSM_IO_F32) | ssm.SSM_DELTA_SOFTPLUS
+    base = {k: to_device(inp[k], torch, dev) for k in ("u", "delta", "B", "C", "z", "A", "D",
+                                                        "delta_bias", "h0")}
+    set_bytes = w.bwd_algorithmic_bytes()
+    nsets = args.sets or max(2, math.ceil(2 * INFINITY_CACHE_BYTES / set_bytes))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 4242)
+    sets = []
+    for i in range(nsets):
+        s = {k: (v if (i == 0 or v is None) else v.clone()) for k, v in base.items()}
+        _, _, s["ckpt"] = ssm.scan_train(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"],
+                                         z=s["z"], delta_bias=s["delta_bias"],
+                                         delta_softplus=True, h0=s["h0"])
+        s["dout"] = torch.randn(s["u"].shape, device=dev, generator=gen).to(io_t)
+        s["dfinal"] = torch.randn((w.batch, w.dim, w.dstate), device=dev, generator=gen)
+        f32 = dict(device=dev, dtype=torch.float32)
+        s.update(du=torch.empty_like(s["u"]), ddelta=torch.empty_like(s["u"]),
+                 dz=None if s["z"] is None else torch.empty_like(s["u"]),
+                 dA=torch.empty((w.dim, w.dstate), **f32),
+                 dB=torch.empty((w.batch, w.dstate, w.seqlen), **f32),
+                 dC=torch.empty((w.batch, w.dstate, w.seqlen), **f32),
+                 dD=torch.empty((w.dim,), **f32), dbias=torch.empty((w.dim,), **f32),
+                 dh0=torch.empty((w.batch, w.dim, w.dstate), **f32))
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()
+    calls = [(ptr(s["u"]), ptr(s["delta"]), ptr(s["A"]), ptr(s["B"]), ptr(s["C"]), ptr(s["D"]),
+              ptr(s["z"]), ptr(s["delta_bias"]), flags, ptr(s["ckpt"]), ptr(s["dout"]),
+              ptr(s["dfinal"]), ptr(s["du"]), ptr(s["ddelta"]), ptr(s["dA"]), ptr(s["dB"]),
+              ptr(s["dC"]), ptr(s["dD"]), ptr(s["dz"]), ptr(s["dbias"]), ptr(s["dh0"]),
+              w.batch, w.dim, w.dstate, w.seqlen, sp) for s in sets]
+    fn = ssm.lib().ssm_scan_bwd
+
+    def launch(i):
+        st = fn(*calls[i % nsets])
+        if st != 0:
+            raise ssm.SsmScanError(st)
+
+    K = args.steps
+    wall, kern_ms = timed_launches(launch, K, args.warmup, stream, torch)
+    avg_ms = float(kern_ms.mean())
+    achieved = set_bytes / (avg_ms * 1e-3) / 1e9
+    alu_achieved = BWD_FLOP_EQ_PER_UPDATE * w.tuples / (avg_ms * 1e-3) / 1e12
+    t_alu = BWD_FLOP_EQ_PER_UPDATE * w.tuples / (ALU_PEAK_TFLOPS * 1e12)
+    t_hbm = set_bytes / (HBM_PEAK_GBS * 1e9)
+    alu = {"achieved": round(alu_achieved, 3), "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(alu_achieved / ALU_PEAK_TFLOPS, 4),
+           "work": (f"{BWD_FLOP_EQ_PER_UPDATE} flop-equivalents per (b,d,n,t) update (18 FMA "
+                    f"issue slots of the sequential adjoint, exp at quarter rate) x {w.tuples}")}
+    hbm = {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4),
+           "work": f"{set_bytes} algorithmic bytes per launch"}
+    main_, other = (("alu", alu), ("hbm", hbm)) if t_alu >= t_hbm else (("hbm", hbm), ("alu", alu))
+    roofline = {"bound": main_[0], **main_[1],
+                "traffic": load_traffic(args.workload, "bwd"), "kernel": "scan_bwd_kernel",
+                "kernel_hash": kernel_hash("bwd"),
+                "floor_us": {"alu": round(t_alu * 1e6, 3), "hbm": round(t_hbm * 1e6, 3)},
+                other[0]: other[1]}
+    value = set_bytes * K / wall / 1e9
+    result = {
+        "metric": f"scan backward GB/s (1 MI355X), {w.describe()}",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64 inputs; dout, dfinal from a seeded torch generator)",
+        "config": {"workload": w.describe(), "direction": "bwd", "batch": w.batch,
+                   "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen, "io_dtype": w.io,
+                   "gate": w.gate, "buffer_sets": nsets, "algorithmic_bytes": set_bytes},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tuples_per_s": round(w.tuples * K / wall, 1),
+        "kernel_us": {"mean": round(avg_ms * 1e3, 3),
+                      "median": round(float(np.median(kern_ms)) * 1e3, 3),
+                      "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                      "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_bwd(w, inp, args.cpu_baseline_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline_bwd(w, inp, budget_s: float):
+    """The backward oracle, untuned, on host cores over the leading channels of batch row 0
+    (all steps), sized to about the time budget."""
+    import oracle
+    from ssm_workloads import widen
+
+    threads = oracle.default_threads()
+    io = inp["io"]
+    rng = np.random.default_rng(w.seed + 4243)
+
+    def timed(nd):
+        sl = lambda x: None if x is None else x[:1, :nd]
+        u = widen(sl(inp["u"]), io)
+        args = (u, widen(sl(inp["delta"]), io), inp["A"][:nd], widen(inp["B"][:1], io),
+                widen(inp["C"][:1], io), inp["D"][:nd], widen(sl(inp["z"]), io),
+                inp["delta_bias"][:nd], True, None if inp["h0"] is None else inp["h0"][:1, :nd])
+        dout = rng.standard_normal(u.shape)
+        t0 = time.perf_counter()
+        oracle.scan_bwd_ref(*args, dout=dout, dfinal=None, nthreads=threads)
+        return time.perf_counter() - t0
+
+    timed(min(w.dim, threads))
+    probe = min(w.dim, max(4 * threads, 64))
+    t_probe = max(timed(probe), 1e-6)
+    nd = max(probe, min(w.dim, int(budget_s / t_probe * probe)))
+    secs = timed(nd)
+    sub = w.with_(batch=1, dim=nd)
+    return {"value": round(sub.bwd_algorithmic_bytes() / secs / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": (f"float64 backward oracle over batch row 0, channels 0..{nd - 1}, all "
+                       f"{w.seqlen} steps ({nd} of {w.batch * w.dim} rows), {secs:.2f} s"),
+            "seconds": round(secs, 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +307,9 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the warm (single set) timing")
+    ap.add_argument("--direction", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: the forward scan (the default, headline); bwd: the backward "
+                         "pass from the forward's saved states")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference, and "
                          "the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -188,6 +338,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(w)
+    if args.direction == "bwd":
+        return bench_bwd(args, w, inp, torch, ssm, dev)
     io_flag = ssm.SSM_IO_BF16 if w.io == "bf16" else ssm.SSM_IO_F32
     flags = io_flag | ssm.SSM_DELTA_SOFTPLUS | (ssm.SSM_INITIAL_STATE if w.initial_state else 0)
 

@@ -55,23 +55,64 @@ struct BParams {
 };
 
 // Inclusive scan from the right: lane i ends with the composition of the operators of
-// lanes i..63, lane 63 applied first: (a, b) <- (a_i a_j, a_i b_j + b_i), j = i + k.
+// lanes i..63, lane 63 applied first: (a, b) <- (a_i a_j, a_i b_j + b_i) for the lanes j
+// to its right.
+//   1. Inside each 16-lane row, four Hillis-Steele steps read the lane k to the right with
+//      DPP row_shl:k (k = 1, 2, 4, 8); a lane whose source is past the row's end is not
+//      written (no bound_ctrl), which is combining with the identity (1, 0).
+//   2. Lane 16 r now holds row r's whole operator. The operators of the rows to the right
+//      of each row are composed from lanes 16, 32 and 48 (read into scalars) and applied
+//      to every lane of the row.
+// gfx950 needs two wait states between a VALU write and a DPP read of the same VGPR.
 __device__ __forceinline__ void wave_scan_from_right(float& a, float& b, int lane) {
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) {
-    const float aj = __shfl_down(a, k, 64);
-    const float bj = __shfl_down(b, k, 64);
-    if (lane + k < 64) {
-      b = __builtin_fmaf(a, bj, b);
-      a = a * aj;
-    }
-  }
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(a), "+v"(b));
+  // row operators (rows 1..3), composed from the right
+  const float a3 = readlane(a, 48), b3 = readlane(b, 48);
+  const float a2 = readlane(a, 32), b2 = readlane(b, 32);
+  const float a1 = readlane(a, 16), b1 = readlane(b, 16);
+  const float s2a = a3, s2b = b3;                                        // rows 3
+  const float s1a = a2 * a3, s1b = __builtin_fmaf(a2, b3, b2);           // rows 2..3
+  const float s0a = a1 * s1a, s0b = __builtin_fmaf(a1, s1b, b1);         // rows 1..3
+  const int row = lane >> 4;
+  float sa = 1.0f, sb = 0.0f;
+  sa = (row == 0) ? s0a : sa;
+  sb = (row == 0) ? s0b : sb;
+  sa = (row == 1) ? s1a : sa;
+  sb = (row == 1) ? s1b : sb;
+  sa = (row == 2) ? s2a : sa;
+  sb = (row == 2) ? s2b : sb;
+  b = __builtin_fmaf(a, sb, b);
+  a = a * sa;
 }
 
+// Lane i receives lane i+1's value; lane 63 receives `last` (DPP wave_shl:1).
+__device__ __forceinline__ float shift_down_one(float v, float last) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(last), __float_as_int(v),
+                                                    0x130, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes, in every lane: DPP row_shr partial sums inside each row (lane 15
+// of a row ends with the row's sum), then the four row sums.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+  return (readlane(v, 15) + readlane(v, 31)) + (readlane(v, 47) + readlane(v, 63));
 }
 
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
@@ -82,11 +123,15 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
   constexpr int kChunk = 64 * T;
   constexpr int kBlocks = T / kVec;
   constexpr uint32_t kEsz = sizeof(Elem);
-  constexpr int kPitch = 65;  // LDS row pitch of the dB/dC sums: [step j][lane]
+  // LDS pitch of the per-wave dB/dC rows, [wave][step j][lane]: 72 = 8 (mod 64) words, so
+  // the 64 lanes of a flush read (8 steps x 8 lanes) fall on 64 different banks.
+  constexpr int kPitch = 72;
   static_assert(kChunk == kCkptInterval, "one interval per saved state");
   static_assert(T % kVec == 0, "whole 16-byte words per lane");
 
-  __shared__ float acc[2][2][T * kPitch];  // [state parity][dB / dC][j * kPitch + lane]
+  // [state parity][dB / dC][wave][j * kPitch + lane]: each wave writes its own rows (no
+  // atomics); the flush adds the K rows of a step.
+  __shared__ float acc[2][2][K][T * kPitch];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,8 +169,9 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
   float dD_acc = 0.0f, db_acc = 0.0f;
 
   {
-    float* flat = &acc[0][0][0];
-    for (int i = tid; i < 2 * 2 * T * kPitch; i += 64 * K) flat[i] = 0.0f;
+    // rows of inactive waves are read by the flush: they stay zero
+    float* flat = &acc[0][0][0][0];
+    for (int i = tid; i < 2 * 2 * K * T * kPitch; i += 64 * K) flat[i] = 0.0f;
   }
   __syncthreads();
 
@@ -242,8 +288,9 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
           for (int j = T - 1; j >= 0; --j) beta = dA[j] * __builtin_fmaf(Cv[j], dyv[j], beta);
           float ra = alpha, rb = beta;
           wave_scan_from_right(ra, rb, lane);
-          const float an = __shfl_down(ra, 1, 64), bn = __shfl_down(rb, 1, 64);
-          float v = (lane == 63) ? G : __builtin_fmaf(an, G, bn);  // e entering from the right
+          // lane 63's right neighbour is the next interval: the identity applied to G
+          const float an = shift_down_one(ra, 1.0f), bn = shift_down_one(rb, 0.0f);
+          float v = __builtin_fmaf(an, G, bn);  // e entering from the right
           const float G_next = __builtin_fmaf(readlane(ra, 0), G, readlane(rb, 0));
           gc_l = (lane == n) ? G_next : gc_l;
           float dAn = 0.0f;
@@ -252,8 +299,8 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
             const float g = __builtin_fmaf(Cv[j], dyv[j], v);  // g_t = C_t dy_t + e_{t+1}
             const float hp = (j > 0) ? h[j - 1] : hin;
             const float t1 = dA[j] * hp;
-            atomicAdd(&acc[par][0][j * kPitch + lane], g * (sv[j] * uv[j]));  // dB
-            atomicAdd(&acc[par][1][j * kPitch + lane], dyv[j] * h[j]);        // dC
+            acc[par][0][wave][j * kPitch + lane] = g * (sv[j] * uv[j]);  // dB
+            acc[par][1][wave][j * kPitch + lane] = dyv[j] * h[j];        // dC
             gdu[j] = __builtin_fmaf(g, sv[j] * Bv[j], gdu[j]);
             gds[j] = __builtin_fmaf(g, __builtin_fmaf(An, t1, Bv[j] * uv[j]), gds[j]);
             dAn = __builtin_fmaf(g * t1, sv[j], dAn);
@@ -263,17 +310,19 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
           dA_l = (lane == n) ? dA_l + dAn : dA_l;
         }
         __syncthreads();  // every channel's share of state n is in acc[par]
-        // Add the workgroup's sums for state n into dB and dC, one step per thread, and
-        // clear the buffer. It is written again two states later, after the next barrier,
-        // which no thread passes before finishing this loop.
+        // Add the workgroup's sums for state n into dB and dC, one step per thread. The
+        // buffer is written again two states later, after the next barrier, which no
+        // thread passes before finishing this loop. Every active wave overwrites its rows
+        // for every state; inactive waves' rows stay zero.
         for (int i = tid; i < kChunk; i += 64 * K) {
           const int ln = i / T, j = i - ln * T;
           const int t = c * kChunk + i;
-          float* sb = &acc[par][0][j * kPitch + ln];
-          float* sc = &acc[par][1][j * kPitch + ln];
-          const float vb = *sb, vc = *sc;
-          *sb = 0.0f;
-          *sc = 0.0f;
+          float vb = 0.0f, vc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            vb += acc[par][0][k][j * kPitch + ln];
+            vc += acc[par][1][k][j * kPitch + ln];
+          }
           if (t < L) {
             const int64_t o = (int64_t(b) * N + n) * L + t;
             unsafeAtomicAdd(&p.dB[o], vb);

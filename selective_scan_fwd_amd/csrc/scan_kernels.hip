@@ -75,7 +75,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // kVecRows: every streamed row starts 16-byte aligned and holds whole 16-byte words.
 // kDmaInputs: u and delta of the next chunk travel by buffer-to-LDS DMA (no registers)
 // instead of a register prefetch.
-template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs>
+// kCkpt: also write the saved states of a training forward (a separate instantiation, so
+// the plain forward carries none of it).
+template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bool kCkpt>
 __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   constexpr int kVec = Vec<Elem>::kN;          // elements per 16-byte word
   constexpr int kChunk = 64 * T;               // steps per chunk
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
         const float carry_out = readlane(bseg, 63);
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
         hc_lane = (lane == n) ? carry_out : hc_lane;
-        if (p.ckpt) {
+        if constexpr (kCkpt) {
           // the state after the first half of the chunk: the last step of the lane before
           // the one whose segment starts at kCkptInterval
           const float mid = readlane(bseg, kCkptInterval / T - 1);
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   for (int c = 0; c < n_chunks; ++c) {
     const int tb = c * kChunk + lane * T;
     sdt = 0.0f;
-    if (p.ckpt && active && lane < N)  // the state entering the chunk
+    if (kCkpt && active && lane < N)  // the state entering the chunk
       p.ckpt[(row * p.n_ckpt + 2 * c) * N + lane] = hc_lane;
     {
       const bool tail = (c + 1) * kChunk > L;
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
       }
     }
     store_lane_block<Elem, kVecRows, T>(out_buf, uint32_t(tb), y);
-    if (p.ckpt && active && lane < N && 2 * c + 1 < p.n_ckpt)
+    if (kCkpt && active && lane < N && 2 * c + 1 < p.n_ckpt)
       p.ckpt[(row * p.n_ckpt + 2 * c + 1) * N + lane] = mid_lane;
   }
 
@@ -405,12 +407,19 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
   p.ckpt = a.ckpt;
   p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
   const int64_t blocks = a.batch * p.dblocks;
-  if (a.vec_ok)
-    hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, true, kDma>), dim3(unsigned(blocks)),
-                       dim3(64 * K), 0, s, p);
-  else
-    hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, false, false>), dim3(unsigned(blocks)),
-                       dim3(64 * K), 0, s, p);
+  const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * K);
+  if (a.vec_ok) {
+    if (a.ckpt)
+      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, true, kDma, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, true, kDma, false>), grid, block, 0, s, p);
+  } else {
+    if (a.ckpt)
+      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, false, false, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, false, false, false>), grid, block, 0, s,
+                         p);
+  }
   return int(hipGetLastError());
 }
 

@@ -71,6 +71,20 @@ class Workload:
             n += self.batch * self.dim * self.dstate * 4             # h0 read
         return n
 
+    def bwd_algorithmic_bytes(self, ckpt_interval: int = 512) -> int:
+        """Bytes the backward pass must move: the forward's inputs, dout, the saved states
+        and dfinal read once; every gradient written once (dB, dC, dA, dD, dbias, dh0 in
+        float32; du, ddelta, dz in the storage type)."""
+        s = 2 if self.io == "bf16" else 4
+        g = 1 if self.gate else 0
+        elems = self.batch * self.dim * self.seqlen
+        n = elems * s * ((3 + g) + (2 + g))                          # u, delta, [z], dout; du, ddelta, [dz]
+        n += self.batch * self.dstate * self.seqlen * 2 * (s + 4)    # B, C read; dB, dC written
+        n += self.dim * self.dstate * 4 * 2 + self.dim * 4 * 4       # A, dA; D, bias, dD, dbias
+        n_ckpt = -(-self.seqlen // ckpt_interval)
+        n += self.batch * self.dim * self.dstate * 4 * (n_ckpt + 2)  # saved states, dfinal, dh0
+        return n
+
     def describe(self) -> str:
         gate = " gated" if self.gate else ""
         h0 = " from-h0" if self.initial_state else ""
