@@ -51,13 +51,13 @@ def _load():
     for name, ct in (("ssm_ref_scan_f64", ctypes.c_double), ("ssm_ref_scan_f32", ctypes.c_float)):
         fn = getattr(lib, name)
         p = ctypes.POINTER(ct)
-        fn.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_int, p, p, p,
+        fn.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_int, p, ctypes.c_void_p, p, p,
                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                        ctypes.c_int]
         fn.restype = ctypes.c_int
     p = ctypes.POINTER(ctypes.c_double)
     fn = lib.ssm_ref_scan_bwd_f64
-    fn.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_int, p, p, p,
+    fn.argtypes = [p, p, p, p, p, p, p, p, ctypes.c_int, p, ctypes.c_void_p, p, p,
                    p, p, p, p, p, p, p, p, p,
                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
     fn.restype = ctypes.c_int
@@ -73,11 +73,22 @@ def default_threads() -> int:
     return max(1, min(n, 16))
 
 
+def _mask_arg(mask, batch, seqlen):
+    """A [batch, seqlen] padding mask as a contiguous uint8 array (None: no padding)."""
+    if mask is None:
+        return None, None
+    m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    if m.shape != (batch, seqlen):
+        raise ValueError("oracle: mask shape")
+    return m, m.ctypes.data_as(ctypes.c_void_p)
+
+
 def scan_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-             h0=None, nthreads: Optional[int] = None, precision: str = "f64"
+             h0=None, nthreads: Optional[int] = None, precision: str = "f64", mask=None
              ) -> Tuple[np.ndarray, np.ndarray]:
     """Sequential selective scan on the CPU. Arrays are real-valued numpy arrays with
-    the shapes given in ssm_ref.h; returns (out [B,D,L], final_state [B,D,N])."""
+    the shapes given in ssm_ref.h; returns (out [B,D,L], final_state [B,D,N]). mask
+    [batch, seqlen] (optional): 0 marks a padding position, where the state is kept."""
     lib = _load()
     dt = np.float64 if precision == "f64" else np.float32
     ct = ctypes.c_double if precision == "f64" else ctypes.c_float
@@ -103,8 +114,9 @@ def scan_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
     def ptr(x):
         return None if x is None else x.ctypes.data_as(ctypes.POINTER(ct))
 
+    m, mp = _mask_arg(mask, batch, seqlen)
     rc = fn(ptr(u), ptr(delta), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z), ptr(delta_bias),
-            1 if delta_softplus else 0, ptr(h0), ptr(out), ptr(fin),
+            1 if delta_softplus else 0, ptr(h0), mp, ptr(out), ptr(fin),
             batch, dim, dstate, seqlen, int(nthreads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle returned {rc}")
@@ -112,7 +124,7 @@ def scan_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=
 
 
 def scan_bwd_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
-                 h0=None, dout=None, dfinal=None, nthreads: Optional[int] = None
+                 h0=None, dout=None, dfinal=None, nthreads: Optional[int] = None, mask=None
                  ) -> Dict[str, Optional[np.ndarray]]:
     """Gradients of L = sum(dout * out) + sum(dfinal * final_state) with respect to every
     input of ``scan_ref`` (float64). Returns a dict with du, ddelta [B,D,L], dA [D,N],
@@ -137,9 +149,10 @@ def scan_bwd_ref(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softp
          "dbias": None if delta_bias is None else np.empty_like(delta_bias),
          "dh0": np.empty((batch, dim, dstate))}
     ptr = lambda x: None if x is None else x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    m, mp = _mask_arg(mask, batch, seqlen)
     rc = lib.ssm_ref_scan_bwd_f64(
         ptr(u), ptr(delta), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z), ptr(delta_bias),
-        1 if delta_softplus else 0, ptr(h0), ptr(dout), ptr(dfinal),
+        1 if delta_softplus else 0, ptr(h0), mp, ptr(dout), ptr(dfinal),
         ptr(g["du"]), ptr(g["ddelta"]), ptr(g["dA"]), ptr(g["dB"]), ptr(g["dC"]),
         ptr(g["dD"]), ptr(g["dz"]), ptr(g["dbias"]), ptr(g["dh0"]),
         batch, dim, dstate, seqlen, int(nthreads or default_threads()))

@@ -11,6 +11,7 @@
  *   for t in 0 .. L-1:
  *       dt   = softplus(delta[b,d,t] + bias[d])                 step size
  *       h[n] = exp(dt * A[d,n]) * h[n] + dt * B[b,n,t] * u[b,d,t]   for each n
+ *       (a padding position, mask[b,t] == 0, keeps h[n] unchanged instead)
  *       y    = sum_n C[b,n,t] * h[n] + D[d] * u[b,d,t]
  *       out[b,d,t] = y * z * sigmoid(z)   (gate present)   or   y
  *   final_state[b,d,n] = h[n]
@@ -25,13 +26,15 @@
  *    engine of Mamba.py", section 3.2 (deltaA = exp(delta*A), deltaB = delta*B,
  *    BX = deltaB*x, y = hs @ C + D*x).
  *  - mhpq.cn/news/1057127, "The hardware truth of Mamba's parallel scan", section 1
- *    (diagonal A: the N state chains are independent).
+ *    (diagonal A: the N state chains are independent), section 4 (a padding mask: at a
+ *    masked position the state is inherited from the previous step, not updated).
  *
  * Readings where the pages are silent or garbled (each is listed with its reason in the
  * design notes): B_bar = delta * B (not the ZOH form); bias is added before softplus;
  * softplus(x) = log1p(exp(x)), returning x above 20; y uses the state after the update;
  * the gate multiplies (C.h + D u) by silu(z) and leaves the state alone; A is [dim, N];
- * B and C are [batch, N, seqlen].
+ * B and C are [batch, N, seqlen]; a masked position still produces an output from the
+ * (unchanged) state, and the mask is per (batch, step), shared by every channel.
  *
  * Parity pins (tests/test_oracle_pins.py) tie this code to the pages' worked examples,
  * closed forms and brute-force expansions. Every function here is pinned.

@@ -28,6 +28,9 @@
  *   step size: ddelta_t = ds_t sig(x_t) with softplus (1 above the threshold 20, where the
  *           forward returns x itself), ds_t without; dbias_d += ddelta_t.
  *   initial state: dh0[n] = a_0[n] g_0[n].
+ * A padding position (mask 0; mhpq.cn/news/1057127 section 4) keeps the state, h_t =
+ * h_{t-1}: there a_t acts as 1, nothing flows into dB, du, dA or ddelta through the state,
+ * and dC and the D and gate terms are as at any other step.
  *
  * The forward states h_t of a row are kept in a per-row buffer (the recomputation the
  * pages mention, done in the plainest way). Channel-summed outputs dB and dC are
@@ -55,7 +58,8 @@ static double sigmoid_ref(double x) { return 1.0 / (1.0 + exp(-x)); }
 int ssm_ref_scan_bwd_f64(const double* u, const double* delta, const double* A,
                          const double* B, const double* C, const double* D, const double* z,
                          const double* delta_bias, int delta_softplus, const double* h0,
-                         const double* dout, const double* dfinal, double* du,
+                         const unsigned char* mask, const double* dout,
+                         const double* dfinal, double* du,
                          double* ddelta, double* dA, double* dB, double* dC, double* dD,
                          double* dz, double* dbias, double* dh0, int64_t batch, int64_t dim,
                          int64_t dstate, int64_t seqlen, int nthreads)
@@ -116,16 +120,19 @@ int ssm_ref_scan_bwd_f64(const double* u, const double* delta, const double* A,
                 for (int64_t t = 0; t < L; ++t) {
                     const double x = dl_r[t] + bias;
                     const double s = delta_softplus ? softplus_ref(x) : x;
+                    const int live = !mask || mask[b * L + t];
                     sv[t] = s;
                     for (int64_t n = 0; n < N; ++n)
-                        hist[(t + 1) * N + n] = exp(s * A_d[n]) * hist[t * N + n] +
-                                                s * B_b[n * L + t] * u_r[t];
+                        hist[(t + 1) * N + n] = live ? exp(s * A_d[n]) * hist[t * N + n] +
+                                                           s * B_b[n * L + t] * u_r[t]
+                                                     : hist[t * N + n];
                 }
 
                 /* backward */
                 for (int64_t n = 0; n < N; ++n) g[n] = dfinal ? dfinal[r * N + n] : 0.0;
                 for (int64_t t = L - 1; t >= 0; --t) {
                     const double s = sv[t], ut = u_r[t];
+                    const int live = !mask || mask[b * L + t];
                     const double* h_t = hist + (t + 1) * N;
                     const double* h_p = hist + t * N;
                     double dy = do_r[t];
@@ -141,9 +148,10 @@ int ssm_ref_scan_bwd_f64(const double* u, const double* delta, const double* A,
                     double ds = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
                         const double Bt = B_b[n * L + t], Ct = C_b[n * L + t];
-                        const double a = exp(s * A_d[n]);
                         g[n] += Ct * dy;                      /* g_t = C_t dy_t + a_{t+1} g_{t+1} */
                         pC_b[n * L + t] += dy * h_t[n];
+                        if (!live) continue;                  /* h_t = h_{t-1}: g passes on */
+                        const double a = exp(s * A_d[n]);
                         pB_b[n * L + t] += g[n] * s * ut;
                         du_t += g[n] * s * Bt;
                         ds += g[n] * (A_d[n] * a * h_p[n] + Bt * ut);

@@ -176,3 +176,43 @@ def test_empty_sequence_passes_the_final_gradient_through():
     g = grads(inp, np.zeros(inp["u"].shape), dfinal, True)
     np.testing.assert_array_equal(g["dh0"], dfinal)
     assert not g["dA"].any() and not g["dD"].any() and not g["dbias"].any()
+
+
+def test_finite_differences_with_padding_mask():
+    """Padding positions (mhpq.cn/news/1057127 section 4) keep the state; the backward
+    oracle must be the derivative of that forward, padding included."""
+    inp = f64_inputs(2, 3, 4, 11, seed=515)
+    rng = np.random.default_rng(516)
+    mask = (rng.random((2, 11)) > 0.35).astype(np.uint8)
+    mask[0, :3] = 0
+    mask[1, -3:] = 0
+    dout = rng.standard_normal(inp["u"].shape)
+    dfinal = rng.standard_normal(inp["h0"].shape)
+
+    def loss_m(i, do, df, sp):
+        out, fin = oracle.scan_ref(i["u"], i["delta"], i["A"], i["B"], i["C"], i["D"], i["z"],
+                                   i["delta_bias"], sp, i["h0"], nthreads=1, mask=mask)
+        return float(np.sum(do * out)) + float(np.sum(df * fin))
+
+    g = oracle.scan_bwd_ref(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                            inp["z"], inp["delta_bias"], True, inp["h0"], dout, dfinal,
+                            nthreads=2, mask=mask)
+    for name in GRAD_OF:
+        x = inp[name]
+        an = g[GRAD_OF[name]]
+        fd = np.empty_like(x)
+        flat, fdf = x.reshape(-1), fd.reshape(-1)
+        for i in range(flat.size):
+            keep = flat[i]
+            eps = 1e-6 * max(1.0, abs(keep))
+            flat[i] = keep + eps
+            lp = loss_m(inp, dout, dfinal, True)
+            flat[i] = keep - eps
+            lm = loss_m(inp, dout, dfinal, True)
+            flat[i] = keep
+            fdf[i] = (lp - lm) / (2 * eps)
+        scale = np.max(np.abs(fd)) + 1e-30
+        err = np.max(np.abs(fd - an)) / scale
+        assert err < 1e-6, f"d/d{name} with mask: max error {err:.2e}"
+    # nothing flows into the step size of a padding position
+    assert not g["ddelta"][np.broadcast_to(mask[:, None, :] == 0, g["ddelta"].shape)].any()

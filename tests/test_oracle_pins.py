@@ -385,3 +385,61 @@ def test_empty_and_degenerate_shapes():
     out, fin = run(np.zeros((0, 3, 5)), np.zeros((0, 3, 5)), A, np.zeros((0, 4, 5)),
                    np.zeros((0, 4, 5)))
     assert out.shape == (0, 3, 5) and fin.shape == (0, 3, 4)
+
+
+# ---------------------------------------------------------------- padding mask
+# mhpq.cn/news/1057127 section 4: at a padding position (mask 0) the state is inherited from
+# the previous step instead of updated; the output there is still C h + D u of that state.
+
+def _masked_case(seed, batch=2, dim=3, N=4, L=40):
+    from ssm_workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["tiny"].with_(batch=batch, dim=dim, dstate=N, seqlen=L, io="f32", gate=True,
+                                initial_state=True, a_kind="scaled", seed=seed)
+    inp = make_inputs(w)
+    f = lambda x: None if x is None else np.asarray(x, np.float64)
+    return {k: f(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")}
+
+
+def _run(inp, mask=None):
+    return oracle.scan_ref(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"],
+                           inp["z"], inp["delta_bias"], True, inp["h0"], mask=mask, nthreads=1)
+
+
+def test_mask_of_ones_is_no_mask():
+    inp = _masked_case(701)
+    a = _run(inp)
+    b = _run(inp, mask=np.ones((2, 40), np.uint8))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_length_mask_is_the_prefix_scan():
+    """mask = (t < len_b): outputs before len_b and the final state are those of the scan
+    of the first len_b steps alone; after len_b the state is frozen and the output is
+    C_t h + D u_t (gated) of that frozen state."""
+    inp = _masked_case(702)
+    lens = [25, 40]
+    mask = np.zeros((2, 40), np.uint8)
+    for b, n in enumerate(lens):
+        mask[b, :n] = 1
+    out, fin = _run(inp, mask)
+    for b, n in enumerate(lens):
+        pre = {k: (v[b:b + 1] if k in ("u", "delta", "z", "B", "C", "h0") else v) for k, v in inp.items()}
+        pre = {k: (v[..., :n] if k in ("u", "delta", "z", "B", "C") else v) for k, v in pre.items()}
+        o, f = _run(pre)
+        assert np.array_equal(out[b, :, :n], o[0]) and np.array_equal(fin[b], f[0])
+        for t in range(n, 40):
+            y = np.einsum("n,dn->d", inp["C"][b, :, t], fin[b]) + inp["D"] * inp["u"][b, :, t]
+            zz = inp["z"][b, :, t]
+            y = y * zz / (1 + np.exp(-zz))
+            np.testing.assert_allclose(out[b, :, t], y, rtol=1e-13, atol=1e-15)
+
+
+def test_interior_padding_is_deleting_those_steps():
+    inp = _masked_case(703, batch=1)
+    rng = np.random.default_rng(704)
+    mask = (rng.random((1, 40)) > 0.3).astype(np.uint8)
+    out, fin = _run(inp, mask)
+    keep = np.nonzero(mask[0])[0]
+    comp = {k: (v[..., keep] if k in ("u", "delta", "z", "B", "C") else v) for k, v in inp.items()}
+    o, f = _run(comp)
+    assert np.array_equal(out[0][:, keep], o[0]) and np.array_equal(fin, f)
