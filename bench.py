@@ -207,7 +207,7 @@ def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
     sp = stream.cuda_stream
     ptr = lambda t: None if t is None else t.data_ptr()
     calls = [(ptr(s["u"]), ptr(s["delta"]), ptr(s["A"]), ptr(s["B"]), ptr(s["C"]), ptr(s["D"]),
-              ptr(s["z"]), ptr(s["delta_bias"]), flags, ptr(s["ckpt"]), ptr(s["dout"]),
+              ptr(s["z"]), ptr(s["delta_bias"]), None, flags, ptr(s["ckpt"]), ptr(s["dout"]),
               ptr(s["dfinal"]), ptr(s["du"]), ptr(s["ddelta"]), ptr(s["dA"]), ptr(s["dB"]),
               ptr(s["dC"]), ptr(s["dD"]), ptr(s["dz"]), ptr(s["dbias"]), ptr(s["dh0"]),
               w.batch, w.dim, w.dstate, w.seqlen, sp) for s in sets]

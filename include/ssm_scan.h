@@ -134,10 +134,26 @@ SSM_API int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, 
                               int64_t dim, int64_t dstate, int64_t seqlen, void* stream);
 
 /*
+ * ssm_scan_fwd_masked -- the forward with a padding mask, and optionally the saved states.
+ * mask: [batch, seqlen] bytes on the device (nullable: no padding). At a step whose byte is
+ * 0 the state is inherited from the previous step instead of updated, as the padding mask
+ * of mhpq.cn/news/1057127 (section 4) does; the output there is still sum_n C h + D u
+ * (gated) of that state, and the step size is not used. The mask is shared by all
+ * channels of a batch row; a per-row length is the mask t < len. chunk_states: as for
+ * ssm_scan_fwd_ckpt, or NULL. Otherwise as ssm_scan_fwd.
+ */
+SSM_API int ssm_scan_fwd_masked(const void* u, const void* delta, const float* A,
+                                const void* B, const void* C, const float* D, const void* z,
+                                const float* delta_bias, const uint8_t* mask, uint32_t flags,
+                                void* out, float* final_state, float* chunk_states,
+                                int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                void* stream);
+
+/*
  * ssm_scan_bwd -- gradients of L = sum(dout * out) + sum(dfinal * final_state) with
  * respect to every input of ssm_scan_fwd.
  *
- * Inputs: the forward's u, delta, A, B, C, D, z, delta_bias and flags (SSM_INITIAL_STATE
+ * Inputs: the forward's u, delta, A, B, C, D, z, delta_bias, mask and flags (SSM_INITIAL_STATE
  * is accepted and has no further effect: the initial state is entry 0 of chunk_states),
  * chunk_states from ssm_scan_fwd_ckpt on the same inputs, dout [batch, dim, seqlen] in the
  * storage type, dfinal fp32 [batch, dim, dstate] (NULL: zero).
@@ -157,7 +173,8 @@ SSM_API int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, 
  */
 SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z,
-                         const float* delta_bias, uint32_t flags, const float* chunk_states,
+                         const float* delta_bias, const uint8_t* mask, uint32_t flags,
+                         const float* chunk_states,
                          const void* dout, const float* dfinal, void* du, void* ddelta,
                          float* dA, float* dB, float* dC, float* dD, void* dz, float* dbias,
                          float* dh0, int64_t batch, int64_t dim, int64_t dstate,
@@ -166,7 +183,7 @@ SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const
 /* Static, human-readable text for a status code (never NULL). */
 SSM_API const char* ssm_scan_strerror(int status);
 
-/* Version of this ABI (bumped on any incompatible change). */
+/* Version of this ABI (bumped on any incompatible change): 2. */
 SSM_API int ssm_scan_abi_version(void);
 
 /*

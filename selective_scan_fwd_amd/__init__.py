@@ -35,7 +35,7 @@ SSM_CKPT_INTERVAL = 512
 
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_strerror", "ssm_scan_abi_version",
             "ssm_scan_debug_wave_combine", "ssm_scan_ckpt_count", "ssm_scan_fwd_ckpt",
-            "ssm_scan_bwd")
+            "ssm_scan_fwd_masked", "ssm_scan_bwd")
 
 _lib = None
 
@@ -70,7 +70,10 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_fwd_ckpt.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
                                     i64, i64, i64, i64, vp]
     L.ssm_scan_fwd_ckpt.restype = ctypes.c_int
-    L.ssm_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
+    L.ssm_scan_fwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp,
+                                      vp, vp, i64, i64, i64, i64, vp]
+    L.ssm_scan_fwd_masked.restype = ctypes.c_int
+    L.ssm_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
                                vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     L.ssm_scan_bwd.restype = ctypes.c_int
     _lib = L
@@ -94,12 +97,19 @@ def ssm_scan_ckpt_count(seqlen: int) -> int:
     return lib().ssm_scan_ckpt_count(seqlen)
 
 
-def ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, flags, chunk_states, dout, dfinal,
+def ssm_scan_fwd_masked(u, delta, A, B, C, D, z, delta_bias, mask, flags, out, final_state,
+                        chunk_states, batch, dim, dstate, seqlen, stream) -> int:
+    return lib().ssm_scan_fwd_masked(u, delta, A, B, C, D, z, delta_bias, mask, flags, out,
+                                     final_state, chunk_states, batch, dim, dstate, seqlen,
+                                     stream)
+
+
+def ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, mask, flags, chunk_states, dout, dfinal,
                  du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch, dim, dstate, seqlen,
                  stream) -> int:
-    return lib().ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, flags, chunk_states, dout,
-                              dfinal, du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch, dim,
-                              dstate, seqlen, stream)
+    return lib().ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, mask, flags, chunk_states,
+                              dout, dfinal, du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch,
+                              dim, dstate, seqlen, stream)
 
 
 def ssm_scan_strerror(status: int) -> str:
@@ -161,11 +171,24 @@ def _check(u, delta, A, B, C, D, z, delta_bias, h0):
     return flags, batch, dim, dstate, seqlen
 
 
+def _check_mask(mask, u, batch, seqlen):
+    import torch
+
+    if mask is None:
+        return None
+    if (tuple(mask.shape) != (batch, seqlen) or mask.dtype not in (torch.uint8, torch.bool)
+            or mask.device != u.device or not mask.is_contiguous()):
+        raise ValueError(f"mask must be a contiguous uint8/bool {(batch, seqlen)} tensor on "
+                         f"{u.device}")
+    return mask
+
+
 def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final_state,
-             return_final_state, save_states):
+             return_final_state, save_states, mask=None):
     import torch
 
     flags, batch, dim, dstate, seqlen = _check(u, delta, A, B, C, D, z, delta_bias, h0)
+    mask = _check_mask(mask, u, batch, seqlen)
     io = u.dtype
     if out is not None and (tuple(out.shape) != tuple(u.shape) or out.dtype != io
                             or out.device != u.device or not out.is_contiguous()):
@@ -194,6 +217,9 @@ def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final
     if save_states:
         states = torch.empty((batch, dim, ssm_scan_ckpt_count(seqlen), dstate), device=u.device,
                              dtype=torch.float32)
+    if mask is not None:
+        status = ssm_scan_fwd_masked(*args[:8], _ptr(mask), *args[8:], _ptr(states), *sizes)
+    elif save_states:
         status = ssm_scan_fwd_ckpt(*args, _ptr(states), *sizes)
     else:
         status = ssm_scan_fwd(*args, *sizes)
@@ -203,29 +229,30 @@ def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final
 
 
 def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
-         h0=None, out=None, final_state=None, return_final_state: bool = True
+         h0=None, out=None, final_state=None, return_final_state: bool = True, mask=None
          ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Selective-scan forward on the GPU.
 
     u, delta, z: [batch, dim, seqlen]; B, C: [batch, dstate, seqlen] (float32 or bfloat16,
     all the same dtype); A: [dim, dstate], D and delta_bias: [dim], h0: [batch, dim,
-    dstate] (float32). Returns (out, final_state); out has u's dtype.
+    dstate] (float32); mask: [batch, seqlen] uint8/bool, 0 = padding step (the state is
+    kept). Returns (out, final_state); out has u's dtype.
     """
     out, fin, _ = _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out,
-                           final_state, return_final_state, False)
+                           final_state, return_final_state, False, mask)
     return out, fin
 
 
 def scan_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
-               h0=None):
+               h0=None, mask=None):
     """``scan`` that also returns the states the backward pass restarts from:
     (out, final_state, chunk_states [batch, dim, ceil(seqlen / 512), dstate] float32)."""
     return _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, None, None, True,
-                    True)
+                    True, mask)
 
 
 def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_bias=None,
-                  delta_softplus: bool = False, dfinal=None, want_dh0: bool = True
+                  delta_softplus: bool = False, dfinal=None, want_dh0: bool = True, mask=None
                   ) -> Dict[str, Optional["torch.Tensor"]]:
     """Gradients of sum(dout * out) + sum(dfinal * final_state) for the forward on the same
     inputs. Returns du, ddelta, dz (u's dtype), dA, dB, dC, dD, dbias, dh0 (float32; None
@@ -233,6 +260,7 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
     import torch
 
     flags, batch, dim, dstate, seqlen = _check(u, delta, A, B, C, D, z, delta_bias, None)
+    mask = _check_mask(mask, u, batch, seqlen)
     n_ck = ssm_scan_ckpt_count(seqlen)
     if (tuple(chunk_states.shape) != (batch, dim, n_ck, dstate)
             or chunk_states.dtype != torch.float32 or not chunk_states.is_contiguous()
@@ -257,7 +285,8 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
          "dbias": None if delta_bias is None else torch.empty((dim,), **f32),
          "dh0": torch.empty((batch, dim, dstate), **f32) if want_dh0 else None}
     status = ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), flags, _ptr(chunk_states), _ptr(dout), _ptr(dfinal),
+                          _ptr(delta_bias), _ptr(mask), flags, _ptr(chunk_states), _ptr(dout),
+                          _ptr(dfinal),
                           _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                           _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dbias"]),
                           _ptr(g["dh0"]), batch, dim, dstate, seqlen, _stream_of(dev))

@@ -36,7 +36,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 extern "C" {
 
-int ssm_scan_abi_version(void) { return 1; }
+int ssm_scan_abi_version(void) { return 2; }
 
 const char* ssm_scan_strerror(int status) {
   switch (status) {
@@ -66,9 +66,9 @@ int64_t ckpt_count(int64_t seqlen) {
 }
 
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
-             const float* D, const void* z, const float* delta_bias, uint32_t flags, void* out,
-             float* final_state, float* ckpt, bool want_ckpt, int64_t batch, int64_t dim,
-             int64_t dstate, int64_t seqlen, void* stream) {
+             const float* D, const void* z, const float* delta_bias, const uint8_t* mask,
+             uint32_t flags, void* out, float* final_state, float* ckpt, bool want_ckpt,
+             int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, void* stream) {
   const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
   if (flags & ~known) return SSM_ERR_INVALID_ARG;
   if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return SSM_ERR_INVALID_ARG;
@@ -121,7 +121,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
         (D && overlaps(o, span(D, dim * 4))) ||
         (delta_bias && overlaps(o, span(delta_bias, dim * 4))) ||
         (final_state && overlaps(o, span(final_state, state_bytes))) ||
-        (ckpt_bytes > 0 && overlaps(o, span(ckpt, ckpt_bytes))))
+        (ckpt_bytes > 0 && overlaps(o, span(ckpt, ckpt_bytes))) ||
+        (mask && overlaps(o, span(mask, batch * seqlen))))
       return SSM_ERR_INVALID_ARG;
   }
 
@@ -154,6 +155,7 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
   a.vec_ok = ((seqlen * esz) % 16 == 0) && aligned(u, 16) && aligned(delta, 16) &&
              aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16));
   a.ckpt = want_ckpt ? ckpt : nullptr;
+  a.mask = mask;
   return ssm::launch_scan_fwd(a, stream) == 0 ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -165,8 +167,17 @@ int ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B
                  const void* C, const float* D, const void* z, const float* delta_bias,
                  uint32_t flags, void* out, float* final_state, int64_t batch, int64_t dim,
                  int64_t dstate, int64_t seqlen, void* stream) {
-  return fwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state, nullptr, false,
-                  batch, dim, dstate, seqlen, stream);
+  return fwd_impl(u, delta, A, B, C, D, z, delta_bias, nullptr, flags, out, final_state,
+                  nullptr, false, batch, dim, dstate, seqlen, stream);
+}
+
+int ssm_scan_fwd_masked(const void* u, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* delta_bias,
+                        const uint8_t* mask, uint32_t flags, void* out, float* final_state,
+                        float* chunk_states, int64_t batch, int64_t dim, int64_t dstate,
+                        int64_t seqlen, void* stream) {
+  return fwd_impl(u, delta, A, B, C, D, z, delta_bias, mask, flags, out, final_state,
+                  chunk_states, chunk_states != nullptr, batch, dim, dstate, seqlen, stream);
 }
 
 int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const void* B,
@@ -174,15 +185,15 @@ int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const vo
                       uint32_t flags, void* out, float* final_state, float* chunk_states,
                       int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                       void* stream) {
-  return fwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, out, final_state, chunk_states,
-                  true, batch, dim, dstate, seqlen, stream);
+  return fwd_impl(u, delta, A, B, C, D, z, delta_bias, nullptr, flags, out, final_state,
+                  chunk_states, true, batch, dim, dstate, seqlen, stream);
 }
 
 int64_t ssm_scan_ckpt_count(int64_t seqlen) { return ckpt_count(seqlen); }
 
 int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* delta_bias,
-                 uint32_t flags, const float* chunk_states, const void* dout,
+                 const uint8_t* mask, uint32_t flags, const float* chunk_states, const void* dout,
                  const float* dfinal, void* du, void* ddelta, float* dA, float* dB, float* dC,
                  float* dD, void* dz, float* dbias, float* dh0, int64_t batch, int64_t dim,
                  int64_t dstate, int64_t seqlen, void* stream) {
@@ -267,6 +278,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.dz = dz;
   a.dbias = delta_bias ? dbias : nullptr;
   a.dh0 = dh0;
+  a.mask = mask;
   a.batch = batch;
   a.dim = dim;
   a.dstate = dstate;

@@ -51,6 +51,7 @@ struct BParams {
   void* dz;
   float* dbias;
   float* dh0;
+  const uint8_t* mask;
   int dim, dstate, seqlen, dblocks, softplus, n_ckpt;
 };
 
@@ -117,7 +118,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
-template <typename Elem, int T, int K, bool kVecRows>
+// kMask: read a padding mask (its own instantiation: the unmasked kernel's register count
+// decides how many waves fit on a SIMD).
+template <typename Elem, int T, int K, bool kVecRows, bool kMask>
 __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
   constexpr int kVec = Vec<Elem>::kN;
   constexpr int kChunk = 64 * T;
@@ -190,6 +193,7 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
     const int tb = c * kChunk + lane * T;
     float uv[T], sv[T], xv[T], dyv[T], gdu[T], gds[T];
     float sdt = 0.0f;
+    uint32_t pad_bits = 0;  // bit j: step tb + j is padding (masked kernels only)
     {
       float dov[T], zv[T];
 #pragma unroll
@@ -205,6 +209,12 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
         xv[j] += bias_d;
         float s = p.softplus ? softplus_f(xv[j]) : xv[j];
         if (tb + j >= L) s = uv[j] = dov[j] = 0.0f;  // past the end: identity steps
+        if constexpr (kMask) {
+          if (tb + j < L && p.mask[int64_t(b) * L + tb + j] == 0) {
+            s = 0.0f;  // padding: the state is kept (the step is the identity)
+            pad_bits |= 1u << j;
+          }
+        }
         sv[j] = s;
         sdt += s;
         dyv[j] = dov[j];
@@ -337,6 +347,9 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
     for (int j = 0; j < T; ++j) {
       const float x = xv[j];
       dd[j] = p.softplus ? gds[j] * sigmoid_f(x) : gds[j];
+      if constexpr (kMask) {
+        if (pad_bits & (1u << j)) dd[j] = 0.0f;  // a padding step's step size is not used
+      }
       if (tb + j < L) db_acc += dd[j];
     }
     store_lane_block<Elem, kVecRows, T>(du_buf, uint32_t(tb), gdu);
@@ -379,6 +392,7 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   p.dz = a.dz;
   p.dbias = a.dbias;
   p.dh0 = a.dh0;
+  p.mask = a.mask;
   p.dim = int(a.dim);
   p.dstate = int(a.dstate);
   p.seqlen = int(a.seqlen);
@@ -386,12 +400,18 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   p.softplus = a.softplus ? 1 : 0;
   p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
   const int64_t blocks = a.batch * p.dblocks;
-  if (a.vec_ok)
-    hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, true>), dim3(unsigned(blocks)), dim3(64 * K),
-                       0, s, p);
-  else
-    hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, false>), dim3(unsigned(blocks)),
-                       dim3(64 * K), 0, s, p);
+  const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * K);
+  if (a.vec_ok) {
+    if (a.mask)
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, true, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, true, false>), grid, block, 0, s, p);
+  } else {
+    if (a.mask)
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, false, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, false, false>), grid, block, 0, s, p);
+  }
   return int(hipGetLastError());
 }
 

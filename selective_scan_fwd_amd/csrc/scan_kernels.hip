@@ -62,6 +62,7 @@ struct KParams {
   void* out;
   float* final_state;
   float* ckpt;  // nullable: states at every kCkptInterval steps, [rows, n_ckpt, dstate]
+  const uint8_t* mask;  // nullable: [batch, seqlen], 0 = padding step (state kept)
   int dim, dstate, seqlen;
   int dblocks;  // ceil(dim / K)
   int softplus, initial_state;
@@ -75,9 +76,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // kVecRows: every streamed row starts 16-byte aligned and holds whole 16-byte words.
 // kDmaInputs: u and delta of the next chunk travel by buffer-to-LDS DMA (no registers)
 // instead of a register prefetch.
-// kCkpt: also write the saved states of a training forward (a separate instantiation, so
-// the plain forward carries none of it).
-template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bool kCkpt>
+// kCkpt: also write the saved states of a training forward; kMask: read a padding mask.
+// Each is a separate instantiation, so the plain forward carries neither (its register
+// count decides how many waves fit on a SIMD).
+template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bool kCkpt,
+          bool kMask>
 __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   constexpr int kVec = Vec<Elem>::kN;          // elements per 16-byte word
   constexpr int kChunk = 64 * T;               // steps per chunk
@@ -315,6 +318,17 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
           y[j] = Dd * uv[e];
         }
       }
+      if constexpr (kMask) {
+        // A padding step keeps the state: a zero step size makes it the identity (dA = 1,
+        // dBu = 0) while y still reads the state.
+        const uint8_t* m = p.mask + int64_t(b) * L;
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const bool live = (tb + j < L) && m[tb + j] != 0;
+          dt[j] = live ? dt[j] : 0.0f;
+          du[j] = live ? du[j] : 0.0f;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < T; ++j) sdt += dt[j];
     }
@@ -385,6 +399,16 @@ __global__ __launch_bounds__(64) void debug_wave_combine_kernel(const float* a, 
   b_out[i] = bv;
 }
 
+template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kMask>
+void launch_flavour(bool ckpt, dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
+  if (ckpt)
+    hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask>), grid, block,
+                       0, s, p);
+  else
+    hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask>), grid,
+                       block, 0, s, p);
+}
+
 template <typename Elem, int T, int K, int G, bool kDma>
 int launch_typed(const FwdArgs& a, hipStream_t s) {
   KParams p;
@@ -405,20 +429,20 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
   p.softplus = a.softplus ? 1 : 0;
   p.initial_state = a.initial_state ? 1 : 0;
   p.ckpt = a.ckpt;
+  p.mask = a.mask;
   p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
   const int64_t blocks = a.batch * p.dblocks;
   const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * K);
   if (a.vec_ok) {
-    if (a.ckpt)
-      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, true, kDma, true>), grid, block, 0, s, p);
+    if (a.mask)
+      launch_flavour<Elem, T, K, G, true, kDma, true>(a.ckpt != nullptr, grid, block, s, p);
     else
-      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, true, kDma, false>), grid, block, 0, s, p);
+      launch_flavour<Elem, T, K, G, true, kDma, false>(a.ckpt != nullptr, grid, block, s, p);
   } else {
-    if (a.ckpt)
-      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, false, false, true>), grid, block, 0, s, p);
+    if (a.mask)
+      launch_flavour<Elem, T, K, G, false, false, true>(a.ckpt != nullptr, grid, block, s, p);
     else
-      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, false, false, false>), grid, block, 0, s,
-                         p);
+      launch_flavour<Elem, T, K, G, false, false, false>(a.ckpt != nullptr, grid, block, s, p);
   }
   return int(hipGetLastError());
 }

@@ -25,6 +25,7 @@ struct FwdArgs {
   bool initial_state;
   bool vec_ok;             // every row of every streamed array starts 16-byte aligned
   float* ckpt = nullptr;   // nullable: states every kCkptInterval steps [rows, n_ckpt, dstate]
+  const uint8_t* mask = nullptr;  // nullable: [batch, seqlen], 0 = padding step
 };
 
 // Spacing of the saved states that the backward pass restarts from (the state entering
@@ -67,6 +68,7 @@ struct BwdArgs {
   void* dz;              // required when z is given
   float* dbias;          // nullable
   float* dh0;            // nullable
+  const uint8_t* mask;   // nullable: [batch, seqlen], 0 = padding step
   int64_t batch, dim, dstate, seqlen;
   Io io;
   bool softplus;

@@ -35,6 +35,7 @@ struct ShortParams {
   void* out;
   float* final_state;
   float* ckpt;   // nullable: [rows, 1, dstate], the state entering step 0
+  const uint8_t* mask;  // nullable: [batch, seqlen], 0 = padding step (state kept)
   int64_t rows;  // batch * dim
   int dim, dstate, seqlen;
   int n2_log2;
@@ -96,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void scan_short_kernel(ShortParams p) {
       bv = load_elem<Elem>(p.B, bc0 + t);
       cv = load_elem<Elem>(p.C, bc0 + t);
     }
-    const float dt = p.softplus ? softplus_f(x) : x;
+    float dt = p.softplus ? softplus_f(x) : x;
+    if (p.mask && p.mask[b * L + t] == 0) dt = 0.0f;  // padding: the state is kept
     h = __builtin_fmaf(exp2_hw(dt * a2), h, (dt * u) * bv);
     float y = cv * h;
     for (int m = n2 >> 1; m > 0; m >>= 1) y += __shfl_xor(y, m, 64);
@@ -124,6 +126,7 @@ int launch_scan_short(const FwdArgs& a, void* stream) {
   p.out = a.out;
   p.final_state = a.final_state;
   p.ckpt = a.ckpt;
+  p.mask = a.mask;
   p.rows = a.batch * a.dim;
   p.dim = int(a.dim);
   p.dstate = int(a.dstate);

@@ -10,6 +10,7 @@ Shapes (all C-contiguous):
     A                : [dim, dstate]  float32
     D, delta_bias    : [dim]          float32
     h0, final_state  : [batch, dim, dstate] float32
+    mask             : [batch, seqlen] uint8 (optional; 0 = padding step)
 """
 from .gen import (
     WORKLOADS,
@@ -17,6 +18,7 @@ from .gen import (
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_inputs,
+    make_mask,
     widen,
 )
 from .compare import RTOL, RTOL_STATE, ParityReport, parity
@@ -25,6 +27,7 @@ __all__ = [
     "WORKLOADS",
     "Workload",
     "make_inputs",
+    "make_mask",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "widen",

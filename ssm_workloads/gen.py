@@ -106,6 +106,34 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+def make_mask(batch: int, seqlen: int, kind: str, seed: int) -> np.ndarray:
+    """A seeded padding mask [batch, seqlen] uint8 (1 = real step, 0 = padding).
+
+    kind "lengths": a batch of sequences of different lengths padded on the right to
+    seqlen (len_b ~ U{1..seqlen}, the last row always full length);
+    "left": the same lengths padded on the left; "random": each step padding with
+    probability 0.3; "ones" / "zeros": all real / all padding.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    m = np.zeros((batch, seqlen), np.uint8)
+    if kind in ("lengths", "left"):
+        lens = rng.integers(1, seqlen + 1, size=batch) if seqlen else np.zeros(batch, int)
+        if batch:
+            lens[-1] = seqlen
+        for b, n in enumerate(lens):
+            if kind == "lengths":
+                m[b, :n] = 1
+            else:
+                m[b, seqlen - n:] = 1
+    elif kind == "random":
+        m[...] = rng.random((batch, seqlen)) >= 0.3
+    elif kind == "ones":
+        m[...] = 1
+    elif kind != "zeros":
+        raise ValueError(f"unknown mask kind {kind!r}")
+    return m
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16, nearest-even; returns the uint16 bit patterns."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)

@@ -56,7 +56,7 @@ def test_header_constants_match_binding():
 
 
 def test_abi_version_and_strerror():
-    assert ssm.ssm_scan_abi_version() == 1
+    assert ssm.ssm_scan_abi_version() == 2
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(ssm.ssm_scan_strerror(s), str) and ssm.ssm_scan_strerror(s)
 
