@@ -7,7 +7,9 @@ imports nothing from the GPU package.
 ``scan_ref`` runs the float64 sequential definition in ``ssm_ref.c`` over whole
 tensors; ``scan_rows`` runs it on selected (batch, channel) rows of a large workload,
 widening only the slices those rows read. ``scan_bwd_ref`` runs the reverse-mode
-derivative of that definition (``ssm_ref_bwd.c``).
+derivative of that definition (``ssm_ref_bwd.c``). ``ssd_ref``, ``ssd_dense_ref`` and
+``ssd_chunked_ref`` (``ssd.py``) are the Mamba-2 (scalar A per head) forward by its
+recurrence, its semiseparable-matrix form and its block decomposition.
 """
 from __future__ import annotations
 
@@ -208,3 +210,6 @@ def sample_rows(batch: int, dim: int, count: int, seed: int) -> Sequence[Tuple[i
     pick = set(rng.choice(total, size=min(count, total), replace=False).tolist())
     pick.update({0, total - 1})
     return [(r // dim, r % dim) for r in sorted(pick)]
+
+
+from .ssd import ssd_chunked_ref, ssd_dense_ref, ssd_ref  # noqa: E402  (uses scan_ref)

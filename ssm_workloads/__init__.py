@@ -11,14 +11,21 @@ Shapes (all C-contiguous):
     D, delta_bias    : [dim]          float32
     h0, final_state  : [batch, dim, dstate] float32
     mask             : [batch, seqlen] uint8 (optional; 0 = padding step)
+
+Mamba-2 (SSD) workloads (``SSD_WORKLOADS``, ``make_ssd_inputs``): x, z, out
+[batch, nheads*headdim, seqlen]; dt [batch, nheads, seqlen]; A, dt_bias [nheads] float32;
+B, C [batch, dstate, seqlen]; D [nheads*headdim] float32.
 """
 from .gen import (
+    SSD_WORKLOADS,
     WORKLOADS,
+    SsdWorkload,
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_inputs,
     make_mask,
+    make_ssd_inputs,
     widen,
 )
 from .compare import RTOL, RTOL_STATE, ParityReport, parity
@@ -26,6 +33,9 @@ from .compare import RTOL, RTOL_STATE, ParityReport, parity
 __all__ = [
     "WORKLOADS",
     "Workload",
+    "SSD_WORKLOADS",
+    "SsdWorkload",
+    "make_ssd_inputs",
     "make_inputs",
     "make_mask",
     "f32_to_bf16_bits",

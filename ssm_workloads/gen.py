@@ -106,6 +106,96 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+@dataclass(frozen=True)
+class SsdWorkload:
+    """A Mamba-2 (SSD) forward: nheads heads of headdim channels, one scalar A and one
+    step size per head, B and C shared by all heads of a batch row."""
+    name: str
+    batch: int
+    nheads: int
+    headdim: int
+    dstate: int
+    seqlen: int
+    io: str = "bf16"
+    gate: bool = True
+    initial_state: bool = False
+    seed: int = 0
+
+    def with_(self, **kw) -> "SsdWorkload":
+        return dataclasses.replace(self, **kw)
+
+    @property
+    def dim(self) -> int:
+        return self.nheads * self.headdim
+
+    def algorithmic_bytes(self) -> int:
+        s = 2 if self.io == "bf16" else 4
+        n = self.batch * self.dim * self.seqlen * s * (2 + (1 if self.gate else 0))  # x, [z], out
+        n += self.batch * self.nheads * self.seqlen * s                 # dt
+        n += self.batch * self.dstate * self.seqlen * 2 * s             # B, C
+        n += self.nheads * 4 * 2 + self.dim * 4                         # A, dt_bias, D
+        n += self.batch * self.dim * self.dstate * 4                    # final_state written
+        if self.initial_state:
+            n += self.batch * self.dim * self.dstate * 4                # h0 read
+        return n
+
+    def describe(self) -> str:
+        gate = " gated" if self.gate else ""
+        h0 = " from-h0" if self.initial_state else ""
+        return (f"{self.name}: b{self.batch} h{self.nheads}x{self.headdim} N{self.dstate} "
+                f"L{self.seqlen} {self.io}{gate}{h0}")
+
+
+SSD_WORKLOADS: Dict[str, SsdWorkload] = {
+    # A Mamba-2 layer's scan at the layer workload's batch, width and length: 32 heads of
+    # 64 channels, 128 states (the larger state the block form makes affordable).
+    "ssd": SsdWorkload("ssd", 4, 32, 64, 128, 2048, "bf16", gate=True, seed=5),
+    "ssd_tiny": SsdWorkload("ssd_tiny", 1, 2, 64, 64, 256, "bf16", gate=True, seed=6),
+}
+
+
+def make_ssd_inputs(w: SsdWorkload) -> Dict[str, Optional[np.ndarray]]:
+    """Draw one SSD workload's inputs (streamed arrays in storage form).
+
+    Draw order (PCG64 seeded with w.seed), each array in C order:
+      1. x      ~ N(0, 1)                  [batch, nheads*headdim, seqlen]
+      2. dt     ~ 0.5 * N(0, 1)            [batch, nheads, seqlen]   (raw)
+      3. dt0    ~ exp(U(log 1e-3, log 1e-1)) [nheads] -> dt_bias = log(expm1(dt0))
+      4. A      = -U(1, 16)                [nheads]
+      5. B      ~ N(0, 1) / sqrt(dstate)   [batch, dstate, seqlen]
+      6. C      ~ N(0, 1) / sqrt(dstate)   [batch, dstate, seqlen]
+      7. D      ~ N(0, 1)                  [nheads*headdim]
+      8. z      ~ N(0, 1)                  [batch, nheads*headdim, seqlen]  (gated only)
+      9. h0     ~ N(0, 1)                  [batch, nheads*headdim, dstate]  (from-h0 only)
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    f32 = np.float32
+    Bn, H, P, N, L = w.batch, w.nheads, w.headdim, w.dstate, w.seqlen
+    x = rng.standard_normal((Bn, H * P, L), dtype=f32)
+    dt = rng.standard_normal((Bn, H, L), dtype=f32) * f32(0.5)
+    dt0 = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=H))
+    dt_bias = np.log(np.expm1(dt0)).astype(f32)
+    A = (-rng.uniform(1.0, 16.0, size=H)).astype(f32)
+    scale = f32(1.0 / np.sqrt(N))
+    Bm = rng.standard_normal((Bn, N, L), dtype=f32) * scale
+    Cm = rng.standard_normal((Bn, N, L), dtype=f32) * scale
+    Dv = rng.standard_normal(H * P, dtype=f32)
+    z = rng.standard_normal((Bn, H * P, L), dtype=f32) if w.gate else None
+    h0 = rng.standard_normal((Bn, H * P, N), dtype=f32) if w.initial_state else None
+    return {
+        "io": w.io,
+        "x": _store(x, w.io),
+        "dt": _store(dt, w.io),
+        "A": A,
+        "B": _store(Bm, w.io),
+        "C": _store(Cm, w.io),
+        "D": Dv,
+        "z": _store(z, w.io) if z is not None else None,
+        "dt_bias": dt_bias,
+        "h0": h0,
+    }
+
+
 def make_mask(batch: int, seqlen: int, kind: str, seed: int) -> np.ndarray:
     """A seeded padding mask [batch, seqlen] uint8 (1 = real step, 0 = padding).
 
