@@ -48,7 +48,10 @@ INFINITY_CACHE_BYTES = 256 << 20
 _CSRC = "selective_scan_fwd_amd/csrc/"
 _SHARED = [_CSRC + "device_math.h", _CSRC + "device_scan.h", _CSRC + "scan_launch.h"]
 KERNEL_SOURCES = {"fwd": [_CSRC + "scan_kernels.hip", _CSRC + "scan_short.hip"] + _SHARED,
-                  "bwd": [_CSRC + "scan_bwd.hip"] + _SHARED}
+                  "bwd": [_CSRC + "scan_bwd.hip"] + _SHARED,
+                  "ssd": [_CSRC + "ssd_kernels.hip"] + _SHARED}
+# Dense bf16 MFMA peak of MI355X (AMD public specification, without sparsity).
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 SHORT_MAX_SEQLEN = 32   # sequences up to this length take the short-sequence kernel
 
 
@@ -65,7 +68,8 @@ def kernel_hash(direction: str = "fwd") -> str:
 def load_traffic(workload: str, direction: str = "fwd"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
     the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"scan_{direction}_{workload}_traffic.json")
+    prefix = {"fwd": "scan_fwd", "bwd": "scan_bwd", "ssd": "ssd_fwd"}[direction]
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -296,6 +300,122 @@ def cpu_baseline_bwd(w, inp, budget_s: float):
             "seconds": round(secs, 3)}
 
 
+def ssd_mfma_flops(w) -> int:
+    """Matrix-core flops one ssm_ssd_fwd call issues (16x16x32 bf16 products of 16384
+    flops): per wave and 64-step block, the carried-state product (4 step tiles x
+    dstate/64 k-blocks x 2 halves), the causal block-diagonal product (3) and the state
+    update (dstate/32 state tiles x 2 k-blocks x 2 halves); 4 waves per 32 channels; plus
+    the prep kernel's G (16 tiles x dstate/32 k-blocks per batch row and block)."""
+    blocks = -(-w.seqlen // 64)
+    per_wave = 4 * (w.dstate // 64) * 2 + 3 + (w.dstate // 32) * 2 * 2
+    waves = 4 * w.batch * w.nheads * (-(-w.headdim // 32))
+    prep = 16 * (w.dstate // 32) * w.batch
+    return 16384 * blocks * (per_wave * waves + prep)
+
+
+def bench_ssd(args, w, torch, ssm, dev) -> int:
+    """The Mamba-2 (SSD) forward: one ssm_ssd_fwd call (prep and block-scan kernels) on
+    resident inputs."""
+    from ssm_workloads import make_ssd_inputs
+
+    inp = make_ssd_inputs(w)
+    flags = ssm.SSM_IO_BF16 | ssm.SSM_DELTA_SOFTPLUS | (ssm.SSM_INITIAL_STATE if w.initial_state else 0)
+    base = {k: to_device(inp[k], torch, dev) for k in ("x", "dt", "B", "C", "z", "A", "D",
+                                                        "dt_bias", "h0")}
+    set_bytes = w.algorithmic_bytes()
+    nsets = args.sets or max(2, math.ceil(2 * INFINITY_CACHE_BYTES / set_bytes))
+    ws_bytes = ssm.ssm_ssd_workspace_bytes(w.batch, w.dstate, w.seqlen)
+    sets = []
+    for i in range(nsets):
+        s = {k: (v if (i == 0 or v is None) else v.clone()) for k, v in base.items()}
+        s["out"] = torch.empty_like(s["x"])
+        s["fin"] = (s["h0"].clone() if s["h0"] is not None
+                    else torch.empty((w.batch, w.dim, w.dstate), device=dev, dtype=torch.float32))
+        s["ws"] = torch.empty((ws_bytes,), device=dev, dtype=torch.uint8)
+        sets.append(s)
+    stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    calls = [(ptr(s["x"]), ptr(s["dt"]), ptr(s["A"]), ptr(s["B"]), ptr(s["C"]), ptr(s["D"]),
+              ptr(s["z"]), ptr(s["dt_bias"]), None, flags, ptr(s["out"]), ptr(s["fin"]),
+              ptr(s["ws"]), ws_bytes, w.batch, w.nheads, w.headdim, w.dstate, w.seqlen,
+              stream.cuda_stream) for s in sets]
+    fn = ssm.lib().ssm_ssd_fwd
+
+    def launch(i):
+        st = fn(*calls[i % nsets])
+        if st != 0:
+            raise ssm.SsmScanError(st)
+
+    K = args.steps
+    wall, kern_ms = timed_launches(launch, K, args.warmup, stream, torch)
+    avg_ms = float(kern_ms.mean())
+    achieved = set_bytes / (avg_ms * 1e-3) / 1e9
+    flops = ssd_mfma_flops(w)
+    t_hbm = set_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    mfma = {"achieved": round(flops / (avg_ms * 1e-3) / 1e12, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(flops / (avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "work": f"{flops} bf16 MFMA flops issued per call"}
+    hbm = {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4),
+           "work": f"{set_bytes} algorithmic bytes per call"}
+    main_, other = (("mfma", mfma), ("hbm", hbm)) if t_mfma >= t_hbm else (("hbm", hbm), ("mfma", mfma))
+    roofline = {"bound": main_[0], **main_[1], "traffic": load_traffic(args.workload, "ssd"),
+                "kernel": "ssd_prep_kernel + ssd_fwd_kernel (one call)",
+                "kernel_hash": kernel_hash("ssd"),
+                "floor_us": {"mfma": round(t_mfma * 1e6, 3), "hbm": round(t_hbm * 1e6, 3)},
+                other[0]: other[1]}
+    value = set_bytes * K / wall / 1e9
+    result = {
+        "metric": f"ssd GB/s & % HBM peak (1 MI355X), {w.describe()}",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64 draws, Mamba-2 initialisation)",
+        "config": {"workload": w.describe(), "batch": w.batch, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "seqlen": w.seqlen,
+                   "io_dtype": w.io, "gate": w.gate, "dt_softplus": True,
+                   "initial_state": w.initial_state, "buffer_sets": nsets,
+                   "algorithmic_bytes": set_bytes},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kernel_us": {"mean": round(avg_ms * 1e3, 3),
+                      "median": round(float(np.median(kern_ms)) * 1e3, 3),
+                      "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+                      "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_ssd(w, inp, args.cpu_baseline_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline_ssd(w, inp, budget_s: float):
+    """The SSD oracle (float64 recurrence), untuned, on host cores: the whole workload,
+    repeated to fill about the time budget."""
+    import oracle
+    from ssm_workloads import widen
+
+    threads = oracle.default_threads()
+    W = lambda k: widen(inp[k], "bf16")
+    args = (W("x"), W("dt"), inp["A"], W("B"), W("C"), inp["D"],
+            None if inp["z"] is None else W("z"), inp["dt_bias"], True, inp["h0"])
+    t0 = time.perf_counter()
+    oracle.ssd_ref(*args, nthreads=threads)
+    one = time.perf_counter() - t0
+    reps = max(1, min(50, int(budget_s / max(one, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.ssd_ref(*args, nthreads=threads)
+    secs = (time.perf_counter() - t0) / reps
+    return {"value": round(w.algorithmic_bytes() / secs / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": (f"float64 recurrence oracle over the whole workload, mean of {reps} "
+                       f"run(s) of {secs:.2f} s"),
+            "seconds": round(secs, 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,10 +449,15 @@ def main() -> int:
         return copy_probe(torch, args.steps, args.warmup)
 
     import selective_scan_fwd_amd as ssm
-    from ssm_workloads import WORKLOADS, make_inputs
+    from ssm_workloads import SSD_WORKLOADS, WORKLOADS, make_inputs
 
+    if args.workload in SSD_WORKLOADS:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        return bench_ssd(args, SSD_WORKLOADS[args.workload], torch, ssm, dev)
     if args.workload not in WORKLOADS:
-        print(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}", file=sys.stderr)
+        print(f"unknown workload {args.workload}; choose from "
+              f"{sorted(WORKLOADS) + sorted(SSD_WORKLOADS)}", file=sys.stderr)
         return 2
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")

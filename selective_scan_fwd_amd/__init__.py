@@ -8,6 +8,8 @@ ABI of include/ssm_scan.h. PyTorch supplies device memory and the current stream
     out, final_state, chunk_states = scan_train(...same arguments...)
     grads = scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None,
                           delta_bias=None, delta_softplus=False, dfinal=None)
+    out, final_state = ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                           dt_softplus=False, h0=None, mask=None)      # Mamba-2, ssm_ssd.h
 
 The ``ssm_scan_*`` functions are the raw C entry points (pointers as ints). If the
 library has not been built this module raises on first use; there is no CPU fallback.
@@ -35,7 +37,7 @@ SSM_CKPT_INTERVAL = 512
 
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_strerror", "ssm_scan_abi_version",
             "ssm_scan_debug_wave_combine", "ssm_scan_ckpt_count", "ssm_scan_fwd_ckpt",
-            "ssm_scan_fwd_masked", "ssm_scan_bwd")
+            "ssm_scan_fwd_masked", "ssm_scan_bwd", "ssm_ssd_workspace_bytes", "ssm_ssd_fwd")
 
 _lib = None
 
@@ -76,6 +78,11 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
                                vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     L.ssm_scan_bwd.restype = ctypes.c_int
+    L.ssm_ssd_workspace_bytes.argtypes = [i64, i64, i64]
+    L.ssm_ssd_workspace_bytes.restype = i64
+    L.ssm_ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
+                              i64, i64, i64, i64, i64, i64, vp]
+    L.ssm_ssd_fwd.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -122,6 +129,17 @@ def ssm_scan_abi_version() -> int:
 
 def ssm_scan_debug_wave_combine(a, b, a_out, b_out, groups, stream) -> int:
     return lib().ssm_scan_debug_wave_combine(a, b, a_out, b_out, groups, stream)
+
+
+def ssm_ssd_workspace_bytes(batch, dstate, seqlen) -> int:
+    return lib().ssm_ssd_workspace_bytes(batch, dstate, seqlen)
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, D, z, dt_bias, mask, flags, out, final_state, workspace,
+                workspace_bytes, batch, nheads, headdim, dstate, seqlen, stream) -> int:
+    return lib().ssm_ssd_fwd(x, dt, A, B, C, D, z, dt_bias, mask, flags, out, final_state,
+                             workspace, workspace_bytes, batch, nheads, headdim, dstate,
+                             seqlen, stream)
 
 
 def _ptr(t) -> Optional[int]:
@@ -293,3 +311,68 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
     if status != SSM_OK:
         raise SsmScanError(status)
     return g
+
+
+def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = False, h0=None,
+        mask=None, out=None, final_state=None, return_final_state: bool = True,
+        workspace=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Mamba-2 (SSD) forward on the GPU: one scalar A and one step size per head.
+
+    x, z: [batch, nheads*headdim, seqlen] bfloat16; dt: [batch, nheads, seqlen] bfloat16;
+    A, dt_bias: [nheads] float32; B, C: [batch, dstate, seqlen] bfloat16; D:
+    [nheads*headdim] float32; h0: [batch, nheads*headdim, dstate] float32; mask:
+    [batch, seqlen] uint8/bool. dstate is 64, 128 or 256 and headdim a multiple of 16.
+    workspace: a uint8 device tensor of at least ssm_ssd_workspace_bytes(...) bytes
+    (allocated per call when None). Returns (out, final_state).
+    """
+    import torch
+
+    if x.dtype != torch.bfloat16:
+        raise TypeError("ssd takes bfloat16 x, dt, B, C and z")
+    if x.dim() != 3 or A.dim() != 1:
+        raise ValueError("x must be [batch, nheads*headdim, seqlen] and A [nheads]")
+    batch, dim, seqlen = x.shape
+    nheads = A.shape[0]
+    if nheads == 0 or dim % nheads:
+        raise ValueError("the channel count must be a multiple of the head count")
+    headdim = dim // nheads
+    dstate = B.shape[1] if B.dim() == 3 else -1
+    want = {"dt": (dt, (batch, nheads, seqlen), torch.bfloat16),
+            "B": (B, (batch, dstate, seqlen), torch.bfloat16),
+            "C": (C, (batch, dstate, seqlen), torch.bfloat16),
+            "A": (A, (nheads,), torch.float32),
+            "z": (z, (batch, dim, seqlen), torch.bfloat16),
+            "D": (D, (dim,), torch.float32),
+            "dt_bias": (dt_bias, (nheads,), torch.float32),
+            "h0": (h0, (batch, dim, dstate), torch.float32)}
+    for name, (t, shape, dtype) in want.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != shape or t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype} {shape}, got {t.dtype} {tuple(t.shape)}")
+        if t.device != x.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {x.device}")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous device tensor")
+    mask = _check_mask(mask, x, batch, seqlen)
+    flags = SSM_IO_BF16 | (SSM_DELTA_SOFTPLUS if dt_softplus else 0)
+    if out is None:
+        out = torch.empty_like(x)
+    if h0 is not None:
+        flags |= SSM_INITIAL_STATE
+        if final_state is None:
+            final_state = h0.clone()
+        elif final_state.data_ptr() != h0.data_ptr():
+            final_state.copy_(h0)
+    elif final_state is None and return_final_state:
+        final_state = torch.empty((batch, dim, dstate), device=x.device, dtype=torch.float32)
+    need = ssm_ssd_workspace_bytes(batch, max(dstate, 0), seqlen)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), device=x.device, dtype=torch.uint8)
+    status = ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                         _ptr(dt_bias), _ptr(mask), flags, _ptr(out), _ptr(final_state),
+                         _ptr(workspace), workspace.numel(), batch, nheads, headdim, dstate,
+                         seqlen, _stream_of(x.device))
+    if status != SSM_OK:
+        raise SsmScanError(status)
+    return out, final_state

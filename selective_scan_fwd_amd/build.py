@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libssmscan.so")
-SOURCES = ["scan_kernels.hip", "scan_short.hip", "scan_bwd.hip", "scan_api.cpp"]
+SOURCES = ["scan_kernels.hip", "scan_short.hip", "scan_bwd.hip", "ssd_kernels.hip", "scan_api.cpp",
+           "ssd_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -111,14 +111,23 @@ struct Buf {
   __device__ uint4 load16(uint32_t off) const {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   }
+  __device__ uint2 load8(uint32_t off) const {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
   __device__ uint32_t load4(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
   __device__ uint32_t load2(uint32_t off) const {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
   }
+  __device__ uint32_t load1(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+  }
   __device__ void store16(uint4 v, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
+  }
+  __device__ void store8(uint2 v, uint32_t off) const {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, off, 0, 0);
   }
   __device__ void store4(uint32_t v, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);

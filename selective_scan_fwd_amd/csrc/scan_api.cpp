@@ -5,32 +5,18 @@
 #include <stdint.h>
 #include <string.h>
 
+#include "api_util.h"
 #include "scan_launch.h"
 #include "ssm_scan.h"
 
 namespace {
 
-constexpr int64_t kInt32Max = 2147483647;
-
-// a * b with overflow detection for non-negative operands.
-bool mul_ok(int64_t a, int64_t b, int64_t* out) {
-  if (a != 0 && b > INT64_MAX / a) return false;
-  *out = a * b;
-  return true;
-}
-
-struct Range {
-  uintptr_t lo, hi;  // [lo, hi)
-};
-
-bool overlaps(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
-
-Range span(const void* p, int64_t bytes) {
-  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
-}
-
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+using ssm_api::aligned;
+using ssm_api::kInt32Max;
+using ssm_api::mul_ok;
+using ssm_api::overlaps;
+using ssm_api::Range;
+using ssm_api::span;
 
 }  // namespace
 

@@ -76,6 +76,32 @@ struct BwdArgs {
 };
 
 int launch_scan_bwd(const BwdArgs& a, void* stream);
+
+// Mamba-2 (SSD) forward: steps per block of the block decomposition.
+constexpr int kSsdBlock = 64;
+
+// Everything an SSD forward launch needs, already validated by the C-ABI layer (bf16
+// storage, dstate in {64, 128, 256}, headdim a multiple of 16, seqlen >= 1).
+struct SsdArgs {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;          // nullable
+  const void* z;           // nullable
+  const float* dt_bias;    // nullable
+  const uint8_t* mask;     // nullable
+  void* out;
+  float* final_state;      // nullable unless initial_state
+  void* workspace;         // G [batch, nblocks, 64, 64] fp32, then C^T [batch, nblocks, 64, dstate] bf16
+  int64_t batch, nheads, headdim, dstate, seqlen;
+  bool softplus;
+  bool initial_state;
+  bool vec_ok;             // rows of x, z, out, B, C hold whole 16-byte words
+};
+
+int launch_ssd_fwd(const SsdArgs& a, void* stream);
 int launch_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
                               int64_t groups, void* stream);
 

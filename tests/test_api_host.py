@@ -13,12 +13,16 @@ import selective_scan_fwd_amd as ssm
 from selective_scan_fwd_amd.build import INCLUDE
 
 HEADER = os.path.join(INCLUDE, "ssm_scan.h")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:SSM_API\s+)?(?:const\s+)?\w+\**\s+\**(ssm_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:SSM_API\s+)?(?:const\s+)?\w+\**\s+\**(ssm_\w+)\s*\(",
+                                text, flags=re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_function():
@@ -122,3 +126,56 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError):
         ssm.scan(x, x, torch.zeros(2, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
+
+
+# ---------------------------------------------------------------- Mamba-2 (SSD) entry
+X, DT, WS = 0x2000000, 0x2100000, 0x2200000
+BF = ssm.SSM_IO_BF16
+
+
+def ssd_call(**kw):
+    args = dict(x=X, dt=DT, A=A, B=B, C=C, D=None, z=None, dt_bias=None, mask=None, flags=BF,
+                out=OUT, final_state=None, workspace=WS, workspace_bytes=1 << 20, batch=2,
+                nheads=2, headdim=32, dstate=64, seqlen=64, stream=None)
+    args.update(kw)
+    return ssm.ssm_ssd_fwd(**args)
+
+
+def test_ssd_workspace_size():
+    # per (batch row, 64-step block): 64x64 fp32 of G and 64 x dstate bf16 of C^T
+    assert ssm.ssm_ssd_workspace_bytes(2, 128, 2048) == 2 * 32 * (64 * 64 * 4 + 64 * 128 * 2)
+    assert ssm.ssm_ssd_workspace_bytes(1, 64, 65) == 2 * (64 * 64 * 4 + 64 * 64 * 2)
+    assert ssm.ssm_ssd_workspace_bytes(3, 64, 0) == 0
+    assert ssm.ssm_ssd_workspace_bytes(-1, 64, 1) == -1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(dt=None), dict(A=None), dict(B=None), dict(out=None),
+    dict(workspace=None), dict(workspace_bytes=1000), dict(batch=-1), dict(seqlen=-1),
+    dict(flags=BF | (1 << 9)), dict(flags=BF | ssm.SSM_INITIAL_STATE),
+    dict(out=X), dict(out=DT), dict(out=WS), dict(out=B + 64),
+])
+def test_ssd_invalid_arguments(kw):
+    assert ssd_call(**kw) == ssm.SSM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(flags=ssm.SSM_IO_F32), dict(dstate=16), dict(dstate=96), dict(dstate=512),
+    dict(headdim=8), dict(headdim=40), dict(seqlen=1 << 31),
+])
+def test_ssd_unsupported(kw):
+    assert ssd_call(**kw) == ssm.SSM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=X + 1), dict(B=B + 1), dict(A=A + 2), dict(workspace=WS + 16),
+    dict(final_state=FIN + 4),
+])
+def test_ssd_misaligned(kw):
+    assert ssd_call(**kw) == ssm.SSM_ERR_MISALIGNED
+
+
+def test_ssd_empty_is_a_noop():
+    assert ssd_call(batch=0) == ssm.SSM_OK
+    assert ssd_call(nheads=0, A=None) == ssm.SSM_OK
+    assert ssd_call(seqlen=0, flags=BF | ssm.SSM_INITIAL_STATE, final_state=FIN) == ssm.SSM_OK
