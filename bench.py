@@ -302,13 +302,16 @@ def cpu_baseline_bwd(w, inp, budget_s: float):
 
 def ssd_mfma_flops(w) -> int:
     """Matrix-core flops one ssm_ssd_fwd call issues (16x16x32 bf16 products of 16384
-    flops): per wave and 64-step block, the carried-state product (4 step tiles x
-    dstate/64 k-blocks x 2 halves), the causal block-diagonal product (3) and the state
-    update (dstate/32 state tiles x 2 k-blocks x 2 halves); 4 waves per 32 channels; plus
-    the prep kernel's G (16 tiles x dstate/32 k-blocks per batch row and block)."""
+    flops). A workgroup of 32 channels runs 2 x ns waves (ns = 4 state splits at 128 states,
+    else 2); per wave and 64-step block: the carried-state product (4 step tiles x its
+    32-state k-blocks x 2 halves), the block-diagonal product (2 per output tile) and the
+    state update (its 16-state tiles x 2 k-blocks x 2 halves). The prep kernel adds G
+    (16 tiles x dstate/32 k-blocks per batch row and block)."""
     blocks = -(-w.seqlen // 64)
-    per_wave = 4 * (w.dstate // 64) * 2 + 3 + (w.dstate // 32) * 2 * 2
-    waves = 4 * w.batch * w.nheads * (-(-w.headdim // 32))
+    ns = 4 if w.dstate == 128 else 2
+    nw = w.dstate // ns
+    per_wave = 4 * (nw // 32) * 2 + 2 * (4 // ns) + (nw // 16) * 2 * 2
+    waves = 2 * ns * w.batch * w.nheads * (-(-w.headdim // 32))
     prep = 16 * (w.dstate // 32) * w.batch
     return 16384 * blocks * (per_wave * waves + prep)
 

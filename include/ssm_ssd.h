@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-/* Bytes of workspace ssm_ssd_fwd needs: per (batch row, 64-step block) 64x64 fp32 for G
+/* Bytes of workspace ssm_ssd_fwd needs: per (batch row, 64-step block) 64x64 bf16 for G
  * and 64 x dstate bf16 for C^T. 0 for empty problems; -1 for negative sizes. */
 SSM_API int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t dstate, int64_t seqlen);
 

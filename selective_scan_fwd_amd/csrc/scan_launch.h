@@ -94,7 +94,7 @@ struct SsdArgs {
   const uint8_t* mask;     // nullable
   void* out;
   float* final_state;      // nullable unless initial_state
-  void* workspace;         // G [batch, nblocks, 64, 64] fp32, then C^T [batch, nblocks, 64, dstate] bf16
+  void* workspace;         // G [batch, nblocks, 64, 64] bf16, then C^T [batch, nblocks, 64, dstate] bf16
   int64_t batch, nheads, headdim, dstate, seqlen;
   bool softplus;
   bool initial_state;

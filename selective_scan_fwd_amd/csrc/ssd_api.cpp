@@ -26,7 +26,7 @@ int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t dstate, int64_t seqlen) {
   int64_t per_block, blocks, total;
   const int64_t q = ssm::kSsdBlock;
   if (!mul_ok(dstate, 2 * q, &per_block) || !mul_ok(batch, nblocks_of(seqlen), &blocks) ||
-      !mul_ok(blocks, q * q * 4 + per_block, &total))
+      !mul_ok(blocks, q * q * 2 + per_block, &total))
     return -1;
   return total;
 }
@@ -57,6 +57,10 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
     return SSM_ERR_UNSUPPORTED;
   need = ssm_ssd_workspace_bytes(batch, dstate, seqlen);
   if (need < 0) return SSM_ERR_UNSUPPORTED;
+  // Both kernels run one-dimensional grids: (batch x blocks) and (batch x heads x groups of
+  // 32 channels) workgroups.
+  if (batch * nblocks_of(seqlen) > kInt32Max || batch * nheads * ((headdim + 31) / 32) > kInt32Max)
+    return SSM_ERR_UNSUPPORTED;
 
   const bool any = elems > 0;
   if ((any && (!x || !dt || !out || !workspace)) || (bc > 0 && (!B || !C)) ||

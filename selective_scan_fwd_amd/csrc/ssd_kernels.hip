@@ -13,8 +13,8 @@
 //
 // Two kernels:
 //   ssd_prep_kernel, one workgroup per (batch row, 64-step block): G = C^T B of the block
-//     (MFMA over the states) and C^T in the lane order the main kernel's operands use.
-//     Both depend only on the batch row, so every head reuses them (from L2).
+//     (MFMA over the states, stored bf16) and C^T in the lane order and swizzle the main
+//     kernel's operands use. Both depend only on the batch row; every head reuses them.
 //   ssd_fwd_kernel, one workgroup per (batch row, head, 32 channels), blocks in order:
 //     the decayed block matrix M = G o exp(cs_t - cs_s) o dt_s (bf16, LDS), then per wave
 //     Y = exp(cs_t) C^T H_in + M x (MFMA), the D skip and gate, and
@@ -22,10 +22,15 @@
 //     that feeds it is an MFMA operand (H_in in the carried-state product, w o x in the
 //     update), it enters as two bf16 halves, hi + lo, which keeps fp32-level accuracy.
 //
-// Wave layout of ssd_fwd_kernel: 4 waves = 2 channel blocks of 16 x 2 halves of the
-// states. A wave holds its (states/2 x 16) slice of H as MFMA accumulators; the two waves
-// of a channel block split the carried-state product over the states and exchange partial
-// outputs through LDS.
+// Wave layout of ssd_fwd_kernel: 2 channel blocks of 16 x kNS splits of the states (kNS = 4
+// for 128 states: 8 waves, two per SIMD; 2 otherwise). A wave holds its slice of H as MFMA
+// accumulators; the waves of a channel block split the carried-state product over the
+// states and sum the partial outputs through LDS.
+//
+// Data movement: the next block's B and C^T (and, up to 128 states, G, x and z) travel by
+// buffer-to-LDS DMA into a second stage while the current block computes, issued in three
+// groups spread over the block, so that the CU's vector memory path (about 64 bytes per
+// clock) works in the background instead of stalling every wave at one point.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 lane layout (checked on the device): lane l, r = l % 16,
 // g = l / 16: A operand row r, k = 8g..8g+7; B operand column r, the same k; result rows
@@ -47,6 +52,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kQ = kSsdBlock;          // steps per block
 constexpr int kMPitch = kQ + 8;        // bf16 per row of the block matrix in LDS
@@ -125,14 +131,25 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v + (row >= 1 ? r0 : 0.0f) + (row >= 2 ? r1 : 0.0f) + (row >= 3 ? r2 : 0.0f);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // XOR swizzle of the 16-byte words of a C^T row in the LDS stage, so that the 16 rows an
 // MFMA operand read touches fall in distinct bank groups (rows of 256 B or more: 16
 // distinct words; rows of 128 B: pairs of rows share a word but not a half).
 template <int N>
 __device__ __forceinline__ int ct_swizzle(int t) {
   return N >= 128 ? (t & 15) : ((t >> 1) & 7);
+}
+
+// The same for 128-byte rows of 64 steps (B, x and z in their LDS stages): word w of row n
+// sits in slot w ^ row_swizzle(n).
+__device__ __forceinline__ int row_swizzle(int n) { return (n >> 1) & 7; }
+
+// The hardware deals workgroups out to the eight XCDs round-robin (workgroup i to XCD
+// i % 8). Renumbering them so that each XCD holds a contiguous range of logical indices
+// puts the workgroups of one batch row, which share G, C^T and B, on as few XCDs (and L2s)
+// as possible.
+__device__ __forceinline__ int xcd_order(int lin, int n) {
+  const int per = n / 8;
+  return lin < 8 * per ? (lin % 8) * per + lin / 8 : lin;
 }
 
 struct SsdParams {
@@ -147,8 +164,8 @@ struct SsdParams {
   const uint8_t* mask;
   uint16_t* out;
   float* final_state;
-  float* G;          // [batch, nblocks, 64, 64]
-  uint16_t* CTp;     // [batch, nblocks, 64, dstate], states in operand order
+  uint16_t* G;       // [batch, nblocks, 64, 64] bf16
+  uint16_t* CTp;     // [batch, nblocks, 64, dstate], states in operand order, swizzled
   int nheads, headdim, seqlen, nblocks;
   int softplus, initial_state;
 };
@@ -160,7 +177,8 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   constexpr int kPitch = N + 8;  // bf16 per LDS row
   __shared__ __attribute__((aligned(16))) uint16_t ct[kQ][kPitch];  // C^T of the block
   __shared__ __attribute__((aligned(16))) uint16_t bt[kQ][kPitch];  // B^T of the block
-  const int c = blockIdx.x, b = blockIdx.y, L = p.seqlen, t0 = c * kQ;
+  const int logical = xcd_order(blockIdx.x, gridDim.x);  // one batch row's blocks together
+  const int c = logical % p.nblocks, b = logical / p.nblocks, L = p.seqlen, t0 = c * kQ;
   const uint32_t bc_bytes = uint32_t(N) * uint32_t(L) * 2u;
   const Buf cbuf(p.C + size_t(b) * N * L, bc_bytes), bbuf(p.B + size_t(b) * N * L, bc_bytes);
 
@@ -181,8 +199,8 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   __syncthreads();
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-  // G[t][s] = sum_n C[n][t] B[n][s]: wave w takes rows 16w..16w+15.
-  float* G = p.G + (size_t(b) * p.nblocks + c) * (kQ * kQ);
+  // G[t][s] = sum_n C[n][t] B[n][s]: wave w takes rows 16w..16w+15 (bf16, row-major).
+  uint16_t* G = p.G + (size_t(b) * p.nblocks + c) * (kQ * kQ);
 #pragma unroll
   for (int sj = 0; sj < kQ / 16; ++sj) {
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -193,7 +211,8 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
       acc = mfma16(a, bv, acc);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) G[(16 * w + 4 * g + i) * kQ + 16 * sj + r] = acc[i];
+    for (int i = 0; i < 4; ++i)
+      G[(16 * w + 4 * g + i) * kQ + 16 * sj + r] = uint16_t(pack_bf16x2(acc[i], 0.0f));
   }
 
   // C^T with the states of each 32-block in operand order (position 8g' + j holds state
@@ -211,45 +230,77 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
 
 // ---------------------------------------------------------------- the block scan
 
+// States split across waves: 128 states in quarters (8 waves, two per SIMD); 64 states in
+// halves (a quarter would be 16, below the 32-deep MFMA); 256 states in halves (its two
+// B and C^T stages alone fill 128 KB of LDS).
+template <int N>
+struct StateSplit {
+  static constexpr int kNS = N == 128 ? 4 : 2;
+  // G, x and z staged in LDS as well (up to 128 states); at 256 they are register loads.
+  static constexpr bool kStageAll = N <= 128;
+};
+
 // Per-lane loads of one block, issued a block ahead of their use into one of two register
 // sets (the block loop is unrolled by two, so the sets alternate without copies).
-template <int N, bool kVec>
+template <int N, bool kVec, int kNS, bool kStageAll>
 struct LaneLoads {
-  static constexpr int kStageWords = kVec ? 1 : N / 32;  // B words staged through registers
+  static constexpr int kWaves = 2 * kNS;                  // 2 channel blocks x kNS state splits
+  static constexpr int kEPT = kQ * kQ / (64 * kWaves);    // block-matrix entries per thread
+  static constexpr int kOwn = 4 / kNS;                    // 16-step output tiles per wave
+  static constexpr int kBInstr = N / 8 / kWaves;          // 1 KB copies of B (and of C^T)
   // dt and the mask byte stay narrow until use: widening them where they are loaded
   // would make the loop carry wait for them (and every memory operation before them).
   uint16_t dt;
   uint8_t live;
-  uint4 g[4];          // G[t][s0 .. s0+15]: this thread's share of the block matrix
-  uint4 xo[2];         // x operands: channel r, steps 32kb + 8g .. +7
-  uint2 xe[2], ze[2];  // x and z at this lane's output positions (its two step tiles)
-  uint4 bst[kStageWords];  // element-wise path: B words bound for the LDS stage
+  // register path (kStageAll false)
+  uint4 g[kStageAll ? 1 : kEPT / 8];       // bf16 G[t][s0 .. s0+kEPT)
+  uint4 xo[kStageAll ? 1 : 2];             // x operands: channel r, steps 32kb + 8g .. +7
+  uint2 xe[kStageAll ? 1 : kOwn], ze[kStageAll ? 1 : kOwn];  // x, z at the output positions
+  // element-wise path (kVec false): words gathered through registers for the LDS stages
+  uint4 bst[kVec ? 1 : kBInstr];
+  uint4 xst[kWaves == 8 ? 1 : 2];
 };
 
-template <int N, bool kVec>
-__global__ __launch_bounds__(256) void ssd_fwd_kernel(SsdParams p) {
-  constexpr int kNH = N / 2, kNT = N / 32, kKB = N / 64;
+template <int N, bool kVec, int kNS>
+__global__ __launch_bounds__(128 * kNS) void ssd_fwd_kernel(SsdParams p) {
+  constexpr bool kStageAll = StateSplit<N>::kStageAll;
+  using LL = LaneLoads<N, kVec, kNS, kStageAll>;
+  constexpr int kWaves = LL::kWaves;
+  constexpr int kNW = N / kNS;                     // states per wave
+  constexpr int kNT = kNW / 16, kKB = kNW / 32;    // its 16-state tiles and 32-state k-blocks
+  constexpr int kOwn = LL::kOwn, kEPT = LL::kEPT, kBInstr = LL::kBInstr;
+  constexpr int kGInstr = 8 / kWaves;              // 1 KB copies of G per wave (kStageAll)
   constexpr int kRowWords = N / 8;                 // 16-byte words per C^T row
-  constexpr int kStageInstr = N / 32;              // 1 KB DMA copies per wave per array
-  // LDS: two stages of B (N x 64 bf16, row = 8 words) and C^T (64 x N bf16), each stage
-  // its own variable and every access to it static: the compiler then knows that reading
-  // one stage does not wait for the DMA filling the other.
+  static_assert(kKB >= 1 && kBInstr >= 1 && kEPT % 8 == 0, "unsupported split");
+  static_assert(kWaves == 4 || kWaves == 8, "x and z copies assume 4 or 8 waves");
+  // LDS: two stages, each array of each stage its own variable and every access to it
+  // static: the compiler then knows that reading one stage does not wait for the DMA
+  // filling the other. B: N x 64 bf16 (row = 8 words); C^T: 64 x N; G: 64 x 64 bf16;
+  // x, z: 32 channels x 64 steps.
+  constexpr int kXW = kStageAll ? 32 * 8 : 1, kGW = kStageAll ? kQ * 8 : 1;
   __shared__ __attribute__((aligned(16))) uint4 sB0[N * 8], sB1[N * 8];
   __shared__ __attribute__((aligned(16))) uint4 sCT0[kQ * kRowWords], sCT1[kQ * kRowWords];
+  __shared__ __attribute__((aligned(16))) uint4 sG0[kGW], sG1[kGW];
+  __shared__ __attribute__((aligned(16))) uint4 sXZ0[2 * kXW], sXZ1[2 * kXW];  // x rows, z rows
   __shared__ __attribute__((aligned(16))) float s_dt[2][kQ], s_cs[2][kQ], s_wdt[2][kQ];
   __shared__ __attribute__((aligned(16))) uint16_t sM[kQ][kMPitch];
-  __shared__ f32x4 sY[4][2][64];
+  __shared__ f32x4 sY[kWaves][4][64];  // partial carried-state products, every step tile
 
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-  const int pb = w & 1, nh = w >> 1;
-  const int pg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // The wave index as a scalar: branches and offsets on it stay wave-uniform.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int pb = w & 1, nq = w >> 1;       // channel block, state split
+  const int pgroups = (p.headdim + 31) / 32;
+  const int logical = xcd_order(blockIdx.x, gridDim.x);
+  const int pg = logical % pgroups, h = (logical / pgroups) % p.nheads;
+  const int b = logical / (pgroups * p.nheads);
   const int P = p.headdim, L = p.seqlen, dim = p.nheads * P;
   const int p0 = pg * 32 + pb * 16;        // first channel (within the head) of this wave
   const bool wave_on = p0 < P;             // headdim % 32 == 16 leaves one block idle
   const int d = h * P + p0 + r;            // this lane's channel (operand column)
-  // Step tiles: this wave finishes tiles nh and nh + 2 (3 causal block products each
-  // way) and hands the partial carried-state product of the other two to its partner.
-  const int own0 = nh, own1 = nh + 2, oth0 = 1 - nh, oth1 = 3 - nh;
+  const int xr = pb * 16 + r;              // its row in the x and z stages
+  // This wave finishes step tiles nq, nq + kNS, ...: with 4 splits one each, with 2 splits
+  // tiles {nq, nq + 2}, 3 of the 6 causal block products either way.
 
   const uint32_t row_bytes = uint32_t(dim) * uint32_t(L) * 2u;
   const Buf xbuf(p.x + size_t(b) * dim * L, row_bytes);
@@ -258,96 +309,133 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(SsdParams p) {
   const Buf bbuf(p.B + size_t(b) * N * L, uint32_t(N) * uint32_t(L) * 2u);
   const Buf dtbuf(p.dt + (size_t(b) * p.nheads + h) * L, uint32_t(L) * 2u);
   const Buf mbuf(p.mask ? p.mask + size_t(b) * L : nullptr, p.mask ? uint32_t(L) : 0u);
-  const uint16_t* CTb = p.CTp + size_t(b) * p.nblocks * (kQ * N);
-  const Buf ctbuf(CTb, uint32_t(p.nblocks) * uint32_t(kQ * N * 2));
+  const Buf ctbuf(p.CTp + size_t(b) * p.nblocks * (kQ * N), uint32_t(p.nblocks) * (kQ * N * 2));
+  const Buf gbuf(p.G + size_t(b) * p.nblocks * (kQ * kQ), uint32_t(p.nblocks) * (kQ * kQ * 2));
   const uint32_t xrow = uint32_t(d) * uint32_t(L);
+  const uint32_t xrow0 = uint32_t(h * P + pg * 32) * uint32_t(L);  // first row of the group
+  const int xvalid = P - pg * 32;          // rows of this group inside the head (16 or more)
 
   const float A_h = p.A[h];
   const float bias_h = p.dt_bias ? p.dt_bias[h] : 0.0f;
   const float D_d = (p.D && wave_on) ? p.D[d] : 0.0f;
 
-  // The state slice of this wave: tile j holds states nh*N/2 + 16j + 4g + i, channel r.
+  // The state slice of this wave: tile j holds states nq*kNW + 16j + 4g + i, channel r.
   f32x4 H[kNT];
   float* fs = p.final_state ? p.final_state + (size_t(b) * dim + d) * N : nullptr;
 #pragma unroll
   for (int j = 0; j < kNT; ++j) {
     H[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (p.initial_state && wave_on)
-      H[j] = *reinterpret_cast<const f32x4*>(fs + nh * kNH + 16 * j + 4 * g);
+      H[j] = *reinterpret_cast<const f32x4*>(fs + nq * kNW + 16 * j + 4 * g);
   }
 
-  const float* Gb = p.G + size_t(b) * p.nblocks * (kQ * kQ);
-  const int mt = threadIdx.x >> 2, ms0 = (threadIdx.x & 3) * 16;  // block-matrix share
+  // Block-matrix share: row mt, columns ms0 .. ms0 + kEPT.
+  const int mt = threadIdx.x / (kQ / kEPT), ms0 = (threadIdx.x % (kQ / kEPT)) * kEPT;
 
-  // B stage word for DMA copy k of this wave: row n = 8 (w kStageInstr + k) + l / 8, slot
-  // l % 8 holding step word (l % 8) ^ ((n >> 1) & 7) of the block (zeros past the end).
-  auto b_stage_offset = [&](int c, int k) -> uint32_t {
-    const int n = 8 * (w * kStageInstr + k) + (l >> 3);
-    const int t = c * kQ + 8 * ((l & 7) ^ ((n >> 1) & 7));
-    return t < L ? 2u * (uint32_t(n) * uint32_t(L) + uint32_t(t)) : kOob;
+  // One 1 KB copy of 8 rows of 64 steps (B, x or z) into a swizzled stage: lane l fills
+  // row 8 k + l / 8, slot l % 8, with step word (l % 8) ^ row_swizzle(row) of block c.
+  // Rows at or past valid_rows and steps past the end read zeros.
+  auto row_copy = [&](const Buf& src, uint32_t row0, int k, int c, uint4* dst, uint4& reg,
+                      int valid_rows) {
+    const int n = 8 * k + (l >> 3);
+    const int t = c * kQ + 8 * ((l & 7) ^ row_swizzle(n));
+    if constexpr (kVec) {
+      const uint32_t off =
+          (t < L && n < valid_rows) ? 2u * (row0 + uint32_t(n) * uint32_t(L) + uint32_t(t)) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_void_t*)&dst[k * 64], 16, off, 0, 0, 0);
+    } else {
+      reg = load8<false>(src, row0 + uint32_t(n) * uint32_t(L), t, n < valid_rows ? L : 0);
+    }
   };
-  // Copy block c's B and C^T into LDS stage c & 1 (DMA; the element-wise path gathers B
-  // through registers and writes it at the start of block c).
-  auto stage_issue = [&](auto tag, int c, LaneLoads<N, kVec>& ld) {
+  // A 1 KB linear copy from the workspace (C^T or G of block c).
+  auto lin_copy = [&](const Buf& src, uint32_t block_bytes, int k, int c, uint4* dst) {
+    const uint32_t off = c < p.nblocks
+                             ? uint32_t(c) * block_bytes + uint32_t(k) * 1024u + uint32_t(l) * 16u
+                             : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_void_t*)&dst[k * 64], 16, off, 0, 0, 0);
+  };
+  // The next block's copies, in three groups spread over the block.
+  auto issue_b = [&](auto tag, int c, LL& ld) {
     uint4* sBs = decltype(tag)::value == 0 ? sB0 : sB1;
-    uint4* sCTs = decltype(tag)::value == 0 ? sCT0 : sCT1;
-    const bool in = c < p.nblocks;
 #pragma unroll
-    for (int k = 0; k < kStageInstr; ++k) {
-      const int idx = w * kStageInstr + k;
-      const uint32_t ct_off =
-          in ? uint32_t(c) * uint32_t(kQ * N * 2) + uint32_t(idx) * 1024u + uint32_t(l) * 16u
-             : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ctbuf.r, (lds_void_t*)&sCTs[idx * 64], 16,
-                                               ct_off, 0, 0, 0);
-      if constexpr (kVec) {
-        const uint32_t off = b_stage_offset(c, k);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(bbuf.r, (lds_void_t*)&sBs[idx * 64], 16, off,
-                                                 0, 0, 0);
-      } else {
-        const int n = 8 * idx + (l >> 3);
-        ld.bst[k] = load8<false>(bbuf, uint32_t(n) * uint32_t(L),
-                                 c * kQ + 8 * ((l & 7) ^ ((n >> 1) & 7)), L);
+    for (int k = 0; k < kBInstr; ++k) row_copy(bbuf, 0u, w * kBInstr + k, c, sBs, ld.bst[k], N);
+  };
+  auto issue_ct_g = [&](auto tag, int c) {
+    uint4* sCTs = decltype(tag)::value == 0 ? sCT0 : sCT1;
+#pragma unroll
+    for (int k = 0; k < kBInstr; ++k) lin_copy(ctbuf, kQ * N * 2, w * kBInstr + k, c, sCTs);
+    if constexpr (kStageAll) {
+      uint4* sGs = decltype(tag)::value == 0 ? sG0 : sG1;
+#pragma unroll
+      for (int k = 0; k < kGInstr; ++k) lin_copy(gbuf, kQ * kQ * 2, w * kGInstr + k, c, sGs);
+    }
+  };
+  auto issue_xz = [&](auto tag, int c, LL& ld) {
+    if constexpr (kStageAll) {
+      uint4* sXZs = decltype(tag)::value == 0 ? sXZ0 : sXZ1;
+      const int zvalid = p.z ? xvalid : 0;
+      if constexpr (kWaves == 8) {  // waves 0..3 copy x, waves 4..7 copy z (no branch)
+        const bool is_z = w >= 4;
+        row_copy(is_z ? zbuf : xbuf, xrow0, w & 3, c, sXZs + (is_z ? kXW : 0), ld.xst[0],
+                 is_z ? zvalid : xvalid);
+      } else {  // every wave copies a quarter of both
+        row_copy(xbuf, xrow0, w, c, sXZs, ld.xst[0], xvalid);
+        row_copy(zbuf, xrow0, w, c, sXZs + kXW, ld.xst[1], zvalid);
       }
     }
   };
-  auto lane_issue = [&](int c, LaneLoads<N, kVec>& ld) {
+  auto lane_issue = [&](int c, LL& ld) {
     const int t0 = c * kQ;
     ld.dt = __builtin_amdgcn_raw_buffer_load_b16(dtbuf.r, t0 + l < L ? 2u * uint32_t(t0 + l) : kOob,
                                                  0, 0);
     ld.live = __builtin_amdgcn_raw_buffer_load_b8(mbuf.r, t0 + l < L ? uint32_t(t0 + l) : kOob, 0,
                                                   0);  // reads 0 without a mask
-    const int cg = c < p.nblocks ? c : c - 1;  // past the last block: a harmless reload
-    const uint4* gp = reinterpret_cast<const uint4*>(Gb + (size_t(cg) * kQ + mt) * kQ + ms0);
+    if constexpr (!kStageAll) {
+      const uint32_t goff =
+          c < p.nblocks ? 2u * (uint32_t(c) * (kQ * kQ) + uint32_t(mt) * kQ + uint32_t(ms0)) : kOob;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ld.g[q] = gp[q];
+      for (int q = 0; q < kEPT / 8; ++q) ld.g[q] = gbuf.load16(c < p.nblocks ? goff + 16u * q : kOob);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) ld.xo[kb] = load8<kVec>(xbuf, xrow, t0 + 32 * kb + 8 * g, L);
-    ld.xe[0] = load4<kVec>(xbuf, xrow, t0 + 16 * own0 + 4 * g, L);
-    ld.xe[1] = load4<kVec>(xbuf, xrow, t0 + 16 * own1 + 4 * g, L);
-    const int tz = p.z ? L : 0;
-    ld.ze[0] = load4<kVec>(zbuf, xrow, t0 + 16 * own0 + 4 * g, tz);
-    ld.ze[1] = load4<kVec>(zbuf, xrow, t0 + 16 * own1 + 4 * g, tz);
+      for (int kb = 0; kb < 2; ++kb) ld.xo[kb] = load8<kVec>(xbuf, xrow, t0 + 32 * kb + 8 * g, L);
+      const int tz = p.z ? L : 0;
+#pragma unroll
+      for (int k = 0; k < kOwn; ++k) {
+        const int te = t0 + 16 * (nq + kNS * k) + 4 * g;
+        ld.xe[k] = load4<kVec>(xbuf, xrow, te, L);
+        ld.ze[k] = load4<kVec>(zbuf, xrow, te, tz);
+      }
+    }
   };
 
-  auto block = [&](auto tag, int c, LaneLoads<N, kVec>& cur, LaneLoads<N, kVec>& nxt) {
+  auto block = [&](auto tag, int c, LL& cur, LL& nxt) {
     constexpr int buf = decltype(tag)::value;  // == c & 1
+    using Next = std::integral_constant<int, buf ^ 1>;
     const uint4* sBb = buf == 0 ? sB0 : sB1;
     const uint4* sCTb = buf == 0 ? sCT0 : sCT1;
+    const uint4* sGb = buf == 0 ? sG0 : sG1;
+    const uint4* sXb = buf == 0 ? sXZ0 : sXZ1;
+    const uint4* sZb = sXb + kXW;
     const int t0 = c * kQ;
-    // This block's DMA (issued during the previous block, before that block's lane loads
-    // and output stores) has landed; the barrier below publishes the stage to all waves.
-    // Vector memory operations complete in issue order, so it suffices to leave the
-    // previous block's output stores outstanding: waiting for them (vmcnt(0)) would expose
-    // their write latency once per block.
-    if constexpr (kVec)
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");  // two 8-byte stores per block
-    else
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // eight 2-byte stores per block
+    // This block's copies (issued during the previous block, before that block's output
+    // stores) have landed; the barrier below publishes the stages to all waves. Vector
+    // memory operations complete in issue order, so it suffices to leave the previous
+    // block's output stores outstanding: waiting for them would expose their write
+    // latency once per block.
+    constexpr int kStores = kOwn * (kVec ? 1 : 4);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStores) : "memory");
     if constexpr (!kVec) {
+      uint4* sBw = buf == 0 ? sB0 : sB1;
 #pragma unroll
-      for (int k = 0; k < kStageInstr; ++k)
-        (buf == 0 ? sB0 : sB1)[(w * kStageInstr + k) * 64 + l] = cur.bst[k];
+      for (int k = 0; k < kBInstr; ++k) sBw[(w * kBInstr + k) * 64 + l] = cur.bst[k];
+      if constexpr (kStageAll) {
+        uint4* sXZw = buf == 0 ? sXZ0 : sXZ1;
+        if constexpr (kWaves == 8) {
+          sXZw[(w >= 4 ? kXW : 0) + (w & 3) * 64 + l] = cur.xst[0];
+        } else {
+          sXZw[w * 64 + l] = cur.xst[0];
+          sXZw[kXW + w * 64 + l] = cur.xst[1];
+        }
+      }
     }
 
     // Step sizes of the block, one per lane; every wave computes them, wave 0 publishes.
@@ -364,37 +452,14 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(SsdParams p) {
     }
     __syncthreads();
 
-    // Unconditional (past the last block the offsets read zeros), so the compiler can
-    // count outstanding loads exactly and never waits for this prefetch inside the block.
-    stage_issue(std::integral_constant<int, buf ^ 1>(), c + 1, nxt);
+    // Prefetch, first group. Unconditional (past the last block the offsets read zeros),
+    // so the compiler can count outstanding loads exactly and never waits for it here.
+    issue_b(Next(), c + 1, nxt);
     lane_issue(c + 1, nxt);
 
-    // Block matrix M[t][s] = G[t][s] exp(cs_t - cs_s) dt_s for s <= t (bf16, LDS).
-    {
-      const float cst = s_cs[buf][mt];
-      float m[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 csq = *reinterpret_cast<const f32x4*>(&s_cs[buf][ms0 + 4 * q]);
-        const f32x4 dtq = *reinterpret_cast<const f32x4*>(&s_dt[buf][ms0 + 4 * q]);
-        const float gq[4] = {__uint_as_float(cur.g[q].x), __uint_as_float(cur.g[q].y),
-                             __uint_as_float(cur.g[q].z), __uint_as_float(cur.g[q].w)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = gq[e] * exp2_hw((cst - csq[e]) * kLog2e) * dtq[e];
-          m[4 * q + e] = ms0 + 4 * q + e <= mt ? v : 0.0f;
-        }
-      }
-      uint32_t mw[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) mw[q] = pack_bf16x2(m[2 * q], m[2 * q + 1]);
-      *reinterpret_cast<uint4*>(&sM[mt][ms0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-      *reinterpret_cast<uint4*>(&sM[mt][ms0 + 8]) = make_uint4(mw[4], mw[5], mw[6], mw[7]);
-    }
-
-    // Carried state: C^T H_in over this wave's half of the states, for all 4 step tiles
-    // (own tiles first). H enters as two bf16 halves (hi + lo): a single bf16 rounding of
-    // the state costs up to 2% of the output where the state dominates it.
+    // Carried state: C^T H_in over this wave's states, for all 4 step tiles. H enters as
+    // two bf16 halves (hi + lo): a single bf16 rounding of the state costs up to 2% of the
+    // output where the state dominates it.
     uint4 hb[kKB], hl[kKB];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
@@ -409,57 +474,113 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(SsdParams p) {
       hb[kb] = make_uint4(whi[0], whi[1], whi[2], whi[3]);
       hl[kb] = make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]);
     }
-    const int tiles[4] = {own0, own1, oth0, oth1};
     f32x4 Y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       Y[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int t = 16 * tiles[i] + r;
+      const int t = 16 * i + r;
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
-        const int slot = (nh * kNH / 8 + 4 * kb + g) ^ ct_swizzle<N>(t);
+        const int slot = (nq * kNW / 8 + 4 * kb + g) ^ ct_swizzle<N>(t);
         const uint4 a = sCTb[t * kRowWords + slot];
         Y[i] = mfma16(a, hb[kb], Y[i]);
         Y[i] = mfma16(a, hl[kb], Y[i]);
       }
     }
-    sY[w][0][l] = Y[2];
-    sY[w][1][l] = Y[3];
+
+    // Prefetch, second group.
+    issue_ct_g(Next(), c + 1);
+
+    // Block matrix M[t][s] = G[t][s] exp(cs_t - cs_s) dt_s for s <= t (bf16, LDS).
+    {
+      const float cst = s_cs[buf][mt];
+      uint4 gw[kEPT / 8];
+#pragma unroll
+      for (int q = 0; q < kEPT / 8; ++q) {
+        if constexpr (kStageAll)
+          gw[q] = sGb[mt * 8 + ms0 / 8 + q];
+        else
+          gw[q] = cur.g[q];
+      }
+      float m[kEPT];
+#pragma unroll
+      for (int q = 0; q < kEPT / 4; ++q) {
+        const f32x4 csq = *reinterpret_cast<const f32x4*>(&s_cs[buf][ms0 + 4 * q]);
+        const f32x4 dtq = *reinterpret_cast<const f32x4*>(&s_dt[buf][ms0 + 4 * q]);
+        const uint4 gg = gw[q >> 1];
+        const uint32_t g01 = (q & 1) ? gg.z : gg.x, g23 = (q & 1) ? gg.w : gg.y;
+        const float gq[4] = {bf16_lo(g01), bf16_hi(g01), bf16_lo(g23), bf16_hi(g23)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = gq[e] * exp2_hw((cst - csq[e]) * kLog2e) * dtq[e];
+          m[4 * q + e] = ms0 + 4 * q + e <= mt ? v : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kEPT / 8; ++q)
+        *reinterpret_cast<uint4*>(&sM[mt][ms0 + 8 * q]) =
+            make_uint4(pack_bf16x2(m[8 * q], m[8 * q + 1]), pack_bf16x2(m[8 * q + 2], m[8 * q + 3]),
+                       pack_bf16x2(m[8 * q + 4], m[8 * q + 5]),
+                       pack_bf16x2(m[8 * q + 6], m[8 * q + 7]));
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sY[w][i][l] = Y[i];
     // A bare barrier: the block matrix and the partial products are LDS writes; a fence
-    // here would also wait for the next block's DMA and lane loads just issued.
+    // here would also wait for the next block's copies just issued.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    f32x4 Yo[2] = {Y[0] + sY[w ^ 2][0][l], Y[1] + sY[w ^ 2][1][l]};
-    // exp(cs_t) on the carried part, then the block-diagonal product on top.
+    // Prefetch, third group: ahead of this block's output stores, so that the wait at the
+    // next block's start can leave exactly those stores outstanding.
+    issue_xz(Next(), c + 1, nxt);
+
+    // x operands of this wave's channels (steps 32kb + 8g .. +7).
+    uint4 xo[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = k == 0 ? own0 : own1;
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (kStageAll)
+        xo[kb] = sXb[xr * 8 + ((4 * kb + g) ^ row_swizzle(xr))];
+      else
+        xo[kb] = cur.xo[kb];
+    }
+
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      const int i = nq + kNS * k;  // this wave's output tile
+      f32x4 Yo = sY[pb][i][l];
+#pragma unroll
+      for (int q = 1; q < kNS; ++q) Yo += sY[pb + 2 * q][i][l];
+      // exp(cs_t) on the carried part, then the block-diagonal product on top.
       const f32x4 csr = *reinterpret_cast<const f32x4*>(&s_cs[buf][16 * i + 4 * g]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Yo[k][q] *= exp2_hw(csr[q] * kLog2e);
+      for (int q = 0; q < 4; ++q) Yo[q] *= exp2_hw(csr[q] * kLog2e);
+      // Both 32-step halves, also for tiles 0 and 1 whose second half of M is zero: a
+      // branch here would cost more than the product (the compiler then also waits for
+      // the DMA in flight before the LDS read inside it).
 #pragma unroll
-      for (int kb = 0; kb <= k; ++kb) {  // tile nh needs steps 0..31, tile nh + 2 all 64
+      for (int kb = 0; kb < 2; ++kb) {
         const uint4 a = *reinterpret_cast<const uint4*>(&sM[16 * i + r][32 * kb + 8 * g]);
-        Yo[k] = mfma16(a, cur.xo[kb], Yo[k]);
+        Yo = mfma16(a, xo[kb], Yo);
       }
-    }
-    // D skip, gate, store: rows t0 + 16 i + 4 g .. +3 of channel d.
-    {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int i = k == 0 ? own0 : own1;
-        const float xv[4] = {bf16_lo(cur.xe[k].x), bf16_hi(cur.xe[k].x), bf16_lo(cur.xe[k].y),
-                             bf16_hi(cur.xe[k].y)};
-        const float zv[4] = {bf16_lo(cur.ze[k].x), bf16_hi(cur.ze[k].x), bf16_lo(cur.ze[k].y),
-                             bf16_hi(cur.ze[k].y)};
-        float y[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          y[q] = Yo[k][q] + D_d * xv[q];
-          if (p.z) y[q] = gate_f(y[q], zv[q]);
-        }
-        store4<kVec>(obuf, xrow, t0 + 16 * i + 4 * g, L, wave_on, y);
+      // D skip, gate, store: rows t0 + 16 i + 4 g .. +3 of channel d.
+      uint2 xe, ze;
+      if constexpr (kStageAll) {
+        const int slot = (2 * i + (g >> 1)) ^ row_swizzle(xr);
+        xe = reinterpret_cast<const uint2*>(&sXb[xr * 8 + slot])[g & 1];
+        ze = reinterpret_cast<const uint2*>(&sZb[xr * 8 + slot])[g & 1];
+      } else {
+        xe = cur.xe[k];
+        ze = cur.ze[k];
       }
+      const float xv[4] = {bf16_lo(xe.x), bf16_hi(xe.x), bf16_lo(xe.y), bf16_hi(xe.y)};
+      const float zv[4] = {bf16_lo(ze.x), bf16_hi(ze.x), bf16_lo(ze.y), bf16_hi(ze.y)};
+      float y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        y[q] = Yo[q] + D_d * xv[q];
+        if (p.z) y[q] = gate_f(y[q], zv[q]);
+      }
+      store4<kVec>(obuf, xrow, t0 + 16 * i + 4 * g, L, wave_on, y);
     }
 
     // State: H <- exp(cs_end) H + B (wdt o x), x scaled per step and split hi + lo.
@@ -472,7 +593,7 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(SsdParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_wdt[buf][32 * kb + 8 * g]);
       const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_wdt[buf][32 * kb + 8 * g + 4]);
-      const uint4 xw = cur.xo[kb];
+      const uint4 xw = xo[kb];
       const float xv[8] = {bf16_lo(xw.x) * w0[0], bf16_hi(xw.x) * w0[1],
                            bf16_lo(xw.y) * w0[2], bf16_hi(xw.y) * w0[3],
                            bf16_lo(xw.z) * w1[0], bf16_hi(xw.z) * w1[1],
@@ -487,17 +608,19 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(SsdParams p) {
       const uint4 xl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
-        const int n = nh * kNH + 16 * j + r;
-        const uint4 a = sBb[n * 8 + ((4 * kb + g) ^ ((n >> 1) & 7))];
+        const int n = nq * kNW + 16 * j + r;
+        const uint4 a = sBb[n * 8 + ((4 * kb + g) ^ row_swizzle(n))];
         H[j] = mfma16(a, xh, H[j]);
         H[j] = mfma16(a, xl, H[j]);
       }
     }
   };
 
-  LaneLoads<N, kVec> la, lb;
-  stage_issue(std::integral_constant<int, 0>(), 0, la);
+  LL la, lb;
+  issue_b(std::integral_constant<int, 0>(), 0, la);
   lane_issue(0, la);
+  issue_ct_g(std::integral_constant<int, 0>(), 0);
+  issue_xz(std::integral_constant<int, 0>(), 0, la);
   for (int c = 0; c < p.nblocks; c += 2) {
     block(std::integral_constant<int, 0>(), c, la, lb);
     if (c + 1 < p.nblocks) block(std::integral_constant<int, 1>(), c + 1, lb, la);
@@ -506,16 +629,17 @@ __global__ __launch_bounds__(256) void ssd_fwd_kernel(SsdParams p) {
   if (fs && wave_on) {
 #pragma unroll
     for (int j = 0; j < kNT; ++j)
-      *reinterpret_cast<f32x4*>(fs + nh * kNH + 16 * j + 4 * g) = H[j];
+      *reinterpret_cast<f32x4*>(fs + nq * kNW + 16 * j + 4 * g) = H[j];
   }
 }
 
 template <int N, bool kVec>
 int launch_n(const SsdArgs& a, const SsdParams& p, hipStream_t s) {
-  const dim3 pgrid = dim3(unsigned(p.nblocks), unsigned(a.batch));
+  constexpr int kNS = StateSplit<N>::kNS;
+  const dim3 pgrid = dim3(unsigned(p.nblocks * a.batch));
   hipLaunchKernelGGL((ssd_prep_kernel<N, kVec>), pgrid, dim3(256), 0, s, p);
-  const dim3 grid = dim3(unsigned((a.headdim + 31) / 32), unsigned(a.nheads), unsigned(a.batch));
-  hipLaunchKernelGGL((ssd_fwd_kernel<N, kVec>), grid, dim3(256), 0, s, p);
+  const dim3 grid = dim3(unsigned((a.headdim + 31) / 32 * a.nheads * a.batch));
+  hipLaunchKernelGGL((ssd_fwd_kernel<N, kVec, kNS>), grid, dim3(128 * kNS), 0, s, p);
   return int(hipGetLastError());
 }
 
@@ -545,9 +669,8 @@ int launch_ssd_fwd(const SsdArgs& a, void* stream) {
   p.nblocks = int((a.seqlen + kQ - 1) / kQ);
   p.softplus = a.softplus ? 1 : 0;
   p.initial_state = a.initial_state ? 1 : 0;
-  p.G = static_cast<float*>(a.workspace);
-  p.CTp = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) +
-                                      size_t(a.batch) * p.nblocks * kQ * kQ * sizeof(float));
+  p.G = static_cast<uint16_t*>(a.workspace);
+  p.CTp = p.G + size_t(a.batch) * p.nblocks * kQ * kQ;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (a.dstate) {
     case 64:

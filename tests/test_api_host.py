@@ -142,9 +142,9 @@ def ssd_call(**kw):
 
 
 def test_ssd_workspace_size():
-    # per (batch row, 64-step block): 64x64 fp32 of G and 64 x dstate bf16 of C^T
-    assert ssm.ssm_ssd_workspace_bytes(2, 128, 2048) == 2 * 32 * (64 * 64 * 4 + 64 * 128 * 2)
-    assert ssm.ssm_ssd_workspace_bytes(1, 64, 65) == 2 * (64 * 64 * 4 + 64 * 64 * 2)
+    # per (batch row, 64-step block): 64x64 bf16 of G and 64 x dstate bf16 of C^T
+    assert ssm.ssm_ssd_workspace_bytes(2, 128, 2048) == 2 * 32 * (64 * 64 * 2 + 64 * 128 * 2)
+    assert ssm.ssm_ssd_workspace_bytes(1, 64, 65) == 2 * (64 * 64 * 2 + 64 * 64 * 2)
     assert ssm.ssm_ssd_workspace_bytes(3, 64, 0) == 0
     assert ssm.ssm_ssd_workspace_bytes(-1, 64, 1) == -1
 
@@ -162,6 +162,7 @@ def test_ssd_invalid_arguments(kw):
 @pytest.mark.parametrize("kw", [
     dict(flags=ssm.SSM_IO_F32), dict(dstate=16), dict(dstate=96), dict(dstate=512),
     dict(headdim=8), dict(headdim=40), dict(seqlen=1 << 31),
+    dict(batch=60000, nheads=60000, headdim=64, seqlen=1),
 ])
 def test_ssd_unsupported(kw):
     assert ssd_call(**kw) == ssm.SSM_ERR_UNSUPPORTED
