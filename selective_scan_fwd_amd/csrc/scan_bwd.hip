@@ -121,7 +121,7 @@ __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_
 // kMask: read a padding mask (its own instantiation: the unmasked kernel's register count
 // decides how many waves fit on a SIMD).
 template <typename Elem, int T, int K, bool kVecRows, bool kMask>
-__global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
+__global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
   constexpr int kVec = Vec<Elem>::kN;
   constexpr int kChunk = 64 * T;
   constexpr int kBlocks = T / kVec;
@@ -206,8 +206,8 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
       }
 #pragma unroll
       for (int j = 0; j < T; ++j) {
-        xv[j] += bias_d;
-        float s = p.softplus ? softplus_f(xv[j]) : xv[j];
+        const float x = xv[j] + bias_d;
+        float s = p.softplus ? softplus_f(x) : x;
         if (tb + j >= L) s = uv[j] = dov[j] = 0.0f;  // past the end: identity steps
         if constexpr (kMask) {
           if (tb + j < L && p.mask[int64_t(b) * L + tb + j] == 0) {
@@ -221,42 +221,17 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
       }
       const float hc_l = (active && lane < N) ? p.ckpt[(row * p.n_ckpt + c) * N + lane] : 0.0f;
 
+      // With the gate, dL/dy = dout z sigmoid(z) does not need y; only dL/dz does, and y
+      // (before the gate) is summed over the states in the loop below, which recomputes
+      // every h_t anyway. dout, z and the biased step size are read again after the loop
+      // (from L2) rather than kept live across it.
+      float y[T];
       if (p.z) {
-        // The gate needs y (before the gate): a forward pass over every state.
-        float y[T];
-#pragma unroll
-        for (int j = 0; j < T; ++j) y[j] = Dd * uv[j];
-        if (active) {
-          for (int n = 0; n < N; ++n) {
-            const float a2 = readlane(a2_l, n), hc = readlane(hc_l, n);
-            float Bv[T], Cv[T], dA[T], dBu[T];
-            load_bc(B_buf, n, tb, Bv);
-            load_bc(C_buf, n, tb, Cv);
-            float bseg = (lane == 0) ? hc : 0.0f;
-#pragma unroll
-            for (int j = 0; j < T; ++j) {
-              dA[j] = exp2_hw(sv[j] * a2);
-              dBu[j] = (sv[j] * uv[j]) * Bv[j];
-              bseg = __builtin_fmaf(dA[j], bseg, dBu[j]);
-            }
-            float aseg = exp2_hw(sdt * a2);
-            wave_scan_inclusive(aseg, bseg);
-            float h = shift_up_one(bseg, hc);
-#pragma unroll
-            for (int j = 0; j < T; ++j) {
-              h = __builtin_fmaf(dA[j], h, dBu[j]);
-              y[j] = __builtin_fmaf(Cv[j], h, y[j]);
-            }
-          }
-        }
-        float dzv[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) {
-          const float sg = sigmoid_f(zv[j]);
-          dzv[j] = dov[j] * y[j] * sg * __builtin_fmaf(zv[j], 1.0f - sg, 1.0f);
-          dyv[j] = dov[j] * zv[j] * sg;
+          dyv[j] = dov[j] * zv[j] * sigmoid_f(zv[j]);
+          y[j] = Dd * uv[j];
         }
-        store_lane_block<Elem, kVecRows, T>(dz_buf, uint32_t(tb), dzv);
       }
 #pragma unroll
       for (int j = 0; j < T; ++j) {
@@ -290,6 +265,7 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
             for (int j = 0; j < T; ++j) {
               hh = __builtin_fmaf(dA[j], hh, (sv[j] * uv[j]) * Bv[j]);
               h[j] = hh;
+              if (p.z) y[j] = __builtin_fmaf(Cv[j], hh, y[j]);
             }
           }
           // adjoint: fold the lane's steps from the right, scan from lane 63 down
@@ -341,11 +317,32 @@ __global__ __launch_bounds__(64 * K) void scan_bwd_kernel(BParams p) {
         }
         ++it;
       }
+      if (p.z) {
+        float dz2[T], zz[T];
+#pragma unroll
+        for (int q = 0; q < kBlocks; ++q) {
+          const uint32_t e = uint32_t(tb + q * kVec);
+          widen_raw16<Elem>(load_word<Elem, kVecRows>(do_buf, e), &dz2[q * kVec]);
+          widen_raw16<Elem>(load_word<Elem, kVecRows>(z_buf, e), &zz[q * kVec]);
+        }
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const float sg = sigmoid_f(zz[j]);
+          dz2[j] = dz2[j] * y[j] * sg * __builtin_fmaf(zz[j], 1.0f - sg, 1.0f);
+        }
+        store_lane_block<Elem, kVecRows, T>(dz_buf, uint32_t(tb), dz2);
+      }
     }
     float dd[T];
+    if (p.softplus) {  // the raw step size again (from L2), for softplus' derivative
+#pragma unroll
+      for (int q = 0; q < kBlocks; ++q)
+        widen_raw16<Elem>(load_word<Elem, kVecRows>(dl_buf, uint32_t(tb + q * kVec)),
+                          &xv[q * kVec]);
+    }
 #pragma unroll
     for (int j = 0; j < T; ++j) {
-      const float x = xv[j];
+      const float x = xv[j] + bias_d;
       dd[j] = p.softplus ? gds[j] * sigmoid_f(x) : gds[j];
       if constexpr (kMask) {
         if (pad_bits & (1u << j)) dd[j] = 0.0f;  // a padding step's step size is not used
