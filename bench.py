@@ -419,6 +419,73 @@ def cpu_baseline_ssd(w, inp, budget_s: float):
             "seconds": round(secs, 3)}
 
 
+def bench_decode_loop(args, w, torch, ssm, dev) -> int:
+    """T one-token forward calls per step, each reading and overwriting one fp32 state
+    tensor (a decode loop over a layer's state cache), timed launched one by one from
+    Python and as one replay of a captured HIP graph. The value is the graph's time per
+    token."""
+    from ssm_workloads import make_inputs
+
+    T = args.decode_loop
+    wl = w.with_(seqlen=T)
+    inp = make_inputs(wl)
+    tok = []
+    for s in range(T):
+        tok.append({k: to_device(np.ascontiguousarray(inp[k][..., s:s + 1]), torch, dev)
+                    for k in ("u", "delta", "B", "C", "z")})
+    par = {k: to_device(inp[k], torch, dev) for k in ("A", "D", "delta_bias", "h0")}
+    state = par["h0"].clone()
+    outs = [torch.empty_like(tok[s]["u"]) for s in range(T)]
+
+    def loop():
+        for s in range(T):
+            g = tok[s]
+            ssm.scan(g["u"], g["delta"], par["A"], g["B"], g["C"], D=par["D"], z=g["z"],
+                     delta_bias=par["delta_bias"], delta_softplus=True, h0=state,
+                     final_state=state, out=outs[s])
+
+    def timed(step, K, W):
+        for _ in range(W):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / K
+
+    K, W = args.steps, args.warmup
+    eager = timed(loop, K, W)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        loop()
+    replay = timed(graph.replay, K, W)
+    tok_bytes = w.algorithmic_bytes()
+    result = {
+        "metric": f"decode loop time per token (1 MI355X), {w.describe()}, HIP graph replay",
+        "value": round(replay / T * 1e6, 3),
+        "unit": "us/token",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(replay * 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64 draws, shapes and distributions of the workload)",
+        "config": {"workload": w.describe(), "tokens_per_step": T, "batch": w.batch,
+                   "dim": w.dim, "dstate": w.dstate, "io_dtype": w.io,
+                   "algorithmic_bytes_per_token": tok_bytes},
+        "eager_us_per_token": round(eager / T * 1e6, 3),
+        "graph_GBps": round(tok_bytes * T / replay / 1e9, 1),
+        "tokens_per_s": round(w.batch * T / replay, 1),
+        "note": "one state tensor is read and rewritten by every call (it stays in the caches "
+                "across tokens); a step is T calls",
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -433,6 +500,9 @@ def main() -> int:
     ap.add_argument("--direction", choices=("fwd", "bwd"), default="fwd",
                     help="fwd: the forward scan (the default, headline); bwd: the backward "
                          "pass from the forward's saved states")
+    ap.add_argument("--decode-loop", type=int, default=0, metavar="T",
+                    help="with --workload decode: time a loop of T one-token calls that carry "
+                         "the state in place, launched eagerly and as one captured HIP graph")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference, and "
                          "the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -465,6 +535,12 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode_loop:
+        if w.seqlen != 1 or not w.initial_state:
+            print("--decode-loop needs a one-step workload from a given state (decode)",
+                  file=sys.stderr)
+            return 2
+        return bench_decode_loop(args, w, torch, ssm, dev)
     inp = make_inputs(w)
     if args.direction == "bwd":
         return bench_bwd(args, w, inp, torch, ssm, dev)

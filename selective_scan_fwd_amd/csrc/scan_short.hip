@@ -8,12 +8,13 @@
 // state-space model: from theory to production CUDA kernel optimisation", section 5.1: the
 // per-layer state cache replaces a growing KV cache; one decode step reads and rewrites it).
 //
-// Mapping: one lane per (channel, state). A channel's states occupy N2 consecutive lanes
-// (N2 = dstate rounded up to a power of two, so a channel never straddles two wavefronts);
-// lanes n >= dstate carry zeros. Each lane walks t = 0..L-1 sequentially with its own state
-// in a register (the recurrence itself, no scan), and y_t is the sum over the channel's
-// lanes of C h (butterfly over N2 lanes). The state is read once (initial state) and
-// written once (final state), both coalesced over n.
+// Mapping: one lane per (channel, four consecutive states), or per (channel, state) when
+// dstate is not a multiple of four or a state pointer is not 16-byte aligned. A channel's
+// lanes are consecutive and a power of two in number, so a channel never straddles two
+// wavefronts; lanes past dstate carry zeros. Each lane walks t = 0..L-1 sequentially with
+// its states in registers (the recurrence itself, no scan), and y_t is the sum over the
+// channel's lanes of C h (butterfly). The state is read once (initial state) and written
+// once (final state), both coalesced over n.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,49 +67,99 @@ __device__ __forceinline__ void store_elem<uint16_t>(void* base, int64_t i, floa
 
 constexpr int kThreads = 256;
 
-template <typename Elem>
+// S consecutive states per lane (S = 1 or 4). With S = 4 the state, A and the saved state
+// move as one 16-byte access per lane, so a decode step needs a quarter of the waves and
+// every wave has four times the bytes in flight.
+template <int S>
+struct Quad {
+  float v[S];
+};
+
+template <int S>
+__device__ __forceinline__ Quad<S> load_states(const float* base, int64_t i) {
+  Quad<S> q;
+  if constexpr (S == 4) {
+    const float4 w = *reinterpret_cast<const float4*>(base + i);
+    q.v[0] = w.x; q.v[1] = w.y; q.v[2] = w.z; q.v[3] = w.w;
+  } else {
+    q.v[0] = base[i];
+  }
+  return q;
+}
+
+template <int S>
+__device__ __forceinline__ void store_states(float* base, int64_t i, const Quad<S>& q) {
+  if constexpr (S == 4) {
+    *reinterpret_cast<float4*>(base + i) = make_float4(q.v[0], q.v[1], q.v[2], q.v[3]);
+  } else {
+    base[i] = q.v[0];
+  }
+}
+
+// Lanes per channel: ceil(dstate / S) rounded up to a power of two (2^lanes_log2 <= 64),
+// so a channel never straddles two wavefronts. Lane j of a channel holds states
+// S*j .. S*j+S-1; with S = 4 the launcher only picks this form when dstate % 4 == 0.
+template <typename Elem, int S>
 __global__ __launch_bounds__(kThreads) void scan_short_kernel(ShortParams p) {
-  const int n2 = 1 << p.n2_log2;
+  const int lanes = 1 << p.n2_log2;
   const int64_t gid = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t row = gid >> p.n2_log2;  // b * dim + d
-  const int n = int(gid & (n2 - 1));
+  const int j = int(gid & (lanes - 1));
+  const int n0 = j * S;
   const bool row_ok = row < p.rows;
-  const bool lane_ok = row_ok && n < p.dstate;
+  const bool lane_ok = row_ok && n0 < p.dstate;
   const int N = p.dstate, L = p.seqlen;
   const int64_t rr = row_ok ? row : 0;
   const int d = int(rr % p.dim);
   const int64_t b = rr / p.dim;
+  const int64_t si = rr * N + (lane_ok ? n0 : 0);  // final_state / ckpt [b, d, n0]
 
-  const float a2 = lane_ok ? p.A[int64_t(d) * N + n] * kLog2e : 0.0f;
+  Quad<S> a2, h;
+  if (lane_ok) {
+    a2 = load_states<S>(p.A, int64_t(d) * N + n0);
+    for (int k = 0; k < S; ++k) a2.v[k] *= kLog2e;
+  } else {
+    for (int k = 0; k < S; ++k) a2.v[k] = 0.0f;
+  }
+  if (lane_ok && p.initial_state) {
+    h = load_states<S>(p.final_state, si);
+  } else {
+    for (int k = 0; k < S; ++k) h.v[k] = 0.0f;
+  }
   const float Dd = (row_ok && p.D) ? p.D[d] : 0.0f;
   const float bias = (row_ok && p.bias) ? p.bias[d] : 0.0f;
-  float h = (lane_ok && p.initial_state) ? p.final_state[rr * N + n] : 0.0f;
-  if (lane_ok && p.ckpt) p.ckpt[rr * N + n] = h;  // seqlen <= 32: one saved state
-  const int64_t bc0 = (b * N + (lane_ok ? n : 0)) * L;  // B[b, n, 0], C[b, n, 0]
-  const int64_t x0 = rr * L;                           // u, delta, z, out [b, d, 0]
+  if (lane_ok && p.ckpt) store_states<S>(p.ckpt, si, h);  // seqlen <= 32: one saved state
+  const int64_t bc0 = (b * N + (lane_ok ? n0 : 0)) * L;  // B[b, n0, 0], C[b, n0, 0]
+  const int64_t x0 = rr * L;                            // u, delta, z, out [b, d, 0]
 
   for (int t = 0; t < L; ++t) {
-    float u = 0.0f, x = 0.0f, bv = 0.0f, cv = 0.0f;
+    // Every load of the step is issued before any arithmetic, the gate's z included.
+    float u = 0.0f, x = 0.0f, zv = 0.0f, bv[S], cv[S];
     if (row_ok) {
       u = load_elem<Elem>(p.u, x0 + t);
       x = load_elem<Elem>(p.delta, x0 + t) + bias;
+      if (p.z) zv = load_elem<Elem>(p.z, x0 + t);
     }
-    if (lane_ok) {
-      bv = load_elem<Elem>(p.B, bc0 + t);
-      cv = load_elem<Elem>(p.C, bc0 + t);
+    for (int k = 0; k < S; ++k) {
+      bv[k] = lane_ok ? load_elem<Elem>(p.B, bc0 + int64_t(k) * L + t) : 0.0f;
+      cv[k] = lane_ok ? load_elem<Elem>(p.C, bc0 + int64_t(k) * L + t) : 0.0f;
     }
     float dt = p.softplus ? softplus_f(x) : x;
     if (p.mask && p.mask[b * L + t] == 0) dt = 0.0f;  // padding: the state is kept
-    h = __builtin_fmaf(exp2_hw(dt * a2), h, (dt * u) * bv);
-    float y = cv * h;
-    for (int m = n2 >> 1; m > 0; m >>= 1) y += __shfl_xor(y, m, 64);
+    const float du = dt * u;
+    float y = 0.0f;
+    for (int k = 0; k < S; ++k) {
+      h.v[k] = __builtin_fmaf(exp2_hw(dt * a2.v[k]), h.v[k], du * bv[k]);
+      y = __builtin_fmaf(cv[k], h.v[k], y);
+    }
+    for (int m = lanes >> 1; m > 0; m >>= 1) y += __shfl_xor(y, m, 64);
     y = __builtin_fmaf(Dd, u, y);
-    if (row_ok && n == 0) {
-      if (p.z) y = gate_f(y, load_elem<Elem>(p.z, x0 + t));
+    if (row_ok && j == 0) {
+      if (p.z) y = gate_f(y, zv);
       store_elem<Elem>(p.out, x0 + t, y);
     }
   }
-  if (lane_ok && p.final_state) p.final_state[rr * N + n] = h;
+  if (lane_ok && p.final_state) store_states<S>(p.final_state, si, h);
 }
 
 }  // namespace
@@ -131,18 +182,31 @@ int launch_scan_short(const FwdArgs& a, void* stream) {
   p.dim = int(a.dim);
   p.dstate = int(a.dstate);
   p.seqlen = int(a.seqlen);
+  // Four states per lane when the state rows split into aligned 16-byte quads.
+  const bool quad = a.dstate % 4 == 0 && reinterpret_cast<uintptr_t>(a.A) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(a.final_state) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(a.ckpt) % 16 == 0;
+  const int64_t per_lane = quad ? 4 : 1;
   int lg = 0;
-  while ((1 << lg) < a.dstate) ++lg;  // dstate <= 64, so lg <= 6
+  while ((int64_t(1) << lg) * per_lane < a.dstate) ++lg;  // dstate <= 64, so lg <= 6
   p.n2_log2 = lg;
   p.softplus = a.softplus ? 1 : 0;
   p.initial_state = a.initial_state ? 1 : 0;
   const int64_t lanes = p.rows << lg;
   const int64_t blocks = (lanes + kThreads - 1) / kThreads;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.io == Io::BF16)
-    hipLaunchKernelGGL(scan_short_kernel<uint16_t>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(scan_short_kernel<float>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, p);
+  const dim3 grid{unsigned(blocks)}, block{unsigned(kThreads)};
+  if (a.io == Io::BF16) {
+    if (quad)
+      hipLaunchKernelGGL((scan_short_kernel<uint16_t, 4>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((scan_short_kernel<uint16_t, 1>), grid, block, 0, s, p);
+  } else {
+    if (quad)
+      hipLaunchKernelGGL((scan_short_kernel<float, 4>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((scan_short_kernel<float, 1>), grid, block, 0, s, p);
+  }
   return int(hipGetLastError());
 }
 

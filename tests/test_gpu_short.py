@@ -1,17 +1,20 @@
 """GPU parity of the short-sequence path (seqlen <= 32: decode and state passing) against
 the float64 oracle, through the C ABI.
 
-Sequences of at most 32 steps run one lane per (channel, state) stepping through time;
-longer ones run the chunked scan. These cases cover that kernel's own mapping: dstate not
-a power of two (idle lanes), 1 and 64 states, channel counts that leave a wavefront
-partly empty, every optional input, the 32/33-step boundary between the two kernels, and
-a decode loop that carries the state from call to call.
+Sequences of at most 32 steps run one lane per (channel, four states) stepping through
+time (one lane per state when dstate is not a multiple of four or a state pointer is not
+16-byte aligned); longer ones run the chunked scan. These cases cover that kernel's own
+mapping: dstate not a power of two or not a multiple of four (idle lanes, the one-state
+form), 1 and 64 states, channel counts that leave a wavefront partly empty, every
+optional input, unaligned state pointers, the 32/33-step boundary between the two
+kernels, and a decode loop that carries the state from call to call.
 """
 import numpy as np
 import pytest
 
 import oracle
-from gpu_util import announce, run_hip
+import selective_scan_fwd_amd as ssm
+from gpu_util import announce, dev, host, run_hip, torch
 from ssm_workloads import RTOL, RTOL_STATE, WORKLOADS, make_inputs, parity, widen
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +43,7 @@ SHORT_SHAPES = [
     # (batch, dim, dstate, seqlen)
     (2, 13, 16, 1), (3, 5, 64, 1), (2, 7, 1, 1), (1, 9, 3, 2), (2, 6, 17, 5),
     (1, 8, 33, 16), (2, 4, 64, 32), (1, 5, 16, 32), (1, 5, 16, 33), (1, 3, 2, 40),
+    (2, 11, 12, 3), (1, 7, 20, 9), (2, 5, 44, 1), (1, 3, 4, 2),
 ]
 
 
@@ -113,3 +117,29 @@ def test_short_zero_input_keeps_only_decay():
     inp = make_inputs(w)
     inp["u"] = np.zeros_like(inp["u"])
     check("f32", run_hip(inp), oracle_full(inp), f"{w.describe()} zero input")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_short_unaligned_state_pointers(io):
+    """A and the state tensors placed 4 bytes past a 16-byte boundary: the kernel falls
+    back from four states per lane to one, with the same results."""
+    t = torch()
+    w = BASE.with_(batch=2, dim=24, dstate=16, seqlen=3, io=io, initial_state=True, seed=45)
+    announce(f"{w.describe()} unaligned A and state")
+    inp = make_inputs(w)
+    g = {k: dev(inp[k], io) for k in ("u", "delta", "B", "C", "z")}
+    f = {k: dev(inp[k], "f32") for k in ("D", "delta_bias")}
+
+    def offset(a):
+        flat = t.empty(a.size + 1, dtype=t.float32, device="cuda")
+        view = flat[1:].view(a.shape)
+        view.copy_(t.from_numpy(np.ascontiguousarray(a, dtype=np.float32)))
+        return view
+
+    A, h0, fin = offset(inp["A"]), offset(inp["h0"]), offset(inp["h0"])
+    assert A.data_ptr() % 16 == 4 and fin.data_ptr() % 16 == 4
+    out, fin = ssm.scan(g["u"], g["delta"], A, g["B"], g["C"], D=f["D"], z=g["z"],
+                        delta_bias=f["delta_bias"], delta_softplus=True, h0=h0,
+                        final_state=fin)
+    t.cuda.synchronize()
+    check(io, (host(out), host(fin)), oracle_full(inp), f"{w.describe()} unaligned")
