@@ -39,6 +39,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
 # slot as one FMA (2 flop), an update is 16 flop-equivalents against the 157.3 peak.
 ALU_PEAK_TFLOPS = 157.3
 FLOP_EQ_PER_UPDATE = 16
+# The 157.3 TFLOP/s figure needs packed fp32 (v_pk_fma_f32: two fp32 FMAs per lane per
+# instruction), which this build disables. Without it a SIMD retires 16 fp32 FMA lanes per
+# clock: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz = 78.6 TFLOP/s, a wave64 v_fma_f32
+# every 4 clocks and a wave64 v_exp_f32 every 8 (bench.py --alu-probe measures both). The
+# same update then costs 4 issue slots plus 2 for the exp: 12 flop-equivalents at 78.6.
+ALU_PEAK_NO_PACKED_TFLOPS = 78.6
+FLOP_EQ_PER_UPDATE_NO_PACKED = 12
 # The backward's minimal work per update (the sequential adjoint): recompute the state
 # (s*A, exp, (s*u)*B, fma: 6 slots), g = C dy + e (1), dC += dy h (1), dB += g s u (1),
 # du += g s B (2), a h_prev (1), ds += g (A a h_prev + B u) (3), dA += g a h_prev s (2),
@@ -157,6 +164,53 @@ def copy_probe(torch, steps: int, warmup: int) -> int:
                       "kernel_us_median": round(float(np.median(ms)) * 1e3, 2),
                       "GBps_read_plus_write": round(2 * n / (float(np.median(ms)) * 1e-3) / 1e9, 1)}),
           flush=True)
+    return 0
+
+
+def alu_probe(torch, steps: int, warmup: int) -> int:
+    """VALU issue rates under this build's flags: independent chains of wave64 v_fma_f32 and
+    of wave64 v_exp_f32 (libssmprobe.so), at 16 waves per CU. Prints one JSON line."""
+    import ctypes
+
+    from selective_scan_fwd_amd.build import PROBE_LIB_PATH
+
+    if not os.path.exists(PROBE_LIB_PATH):
+        raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build first")
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    lib.ssm_probe_alu.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.ssm_probe_alu.restype = ctypes.c_int
+    lib.ssm_probe_ops_per_launch.argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.ssm_probe_ops_per_launch.restype = ctypes.c_int64
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    blocks, iters = cus * 4, 200            # 4 workgroups of 4 waves: 16 waves per CU
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {"probe": "alu", "cus": cus, "waves_per_cu": 16,
+           "note": "packed fp32 disabled at build time; lane-ops per second, and clocks per "
+                   "wave64 instruction per SIMD at the 2.4 GHz peak clock"}
+    for kind, name in ((0, "v_fma_f32"), (1, "v_exp_f32")):
+        launch = lambda: lib.ssm_probe_alu(kind, blocks, iters, out.data_ptr(),
+                                           stream.cuda_stream)
+        for _ in range(warmup):
+            if launch() != 0:
+                raise RuntimeError("probe launch failed")
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            launch()
+        b.record(stream)
+        torch.cuda.synchronize()
+        sec = a.elapsed_time(b) * 1e-3 / steps
+        ops = lib.ssm_probe_ops_per_launch(blocks, iters)
+        wave_instr_per_simd = ops / 64 / (cus * 4)
+        res[name] = {"lane_ops_per_s": round(ops / sec, 1),
+                     "clk_per_wave_instr_at_2p4GHz": round(sec * 2.4e9 / wave_instr_per_simd, 3)}
+    fma = res["v_fma_f32"]["lane_ops_per_s"]
+    res["v_fma_f32"]["TFLOPs"] = round(2 * fma / 1e12, 2)
+    print(json.dumps(res), flush=True)
     return 0
 
 
@@ -503,6 +557,9 @@ def main() -> int:
     ap.add_argument("--decode-loop", type=int, default=0, metavar="T",
                     help="with --workload decode: time a loop of T one-token calls that carry "
                          "the state in place, launched eagerly and as one captured HIP graph")
+    ap.add_argument("--alu-probe", action="store_true",
+                    help="measure the issue rates of wave64 v_fma_f32 and v_exp_f32 under this "
+                         "build's flags (register-only probe kernels)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (HBM reference, and "
                          "the known-size kernel that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -520,6 +577,8 @@ def main() -> int:
 
     if args.copy_probe:
         return copy_probe(torch, args.steps, args.warmup)
+    if args.alu_probe:
+        return alu_probe(torch, min(args.steps, 20), min(args.warmup, 3))
 
     import selective_scan_fwd_amd as ssm
     from ssm_workloads import SSD_WORKLOADS, WORKLOADS, make_inputs
@@ -628,6 +687,17 @@ def main() -> int:
                 "kernel_hash": kernel_hash(),
                 "floor_us": {"alu": round(t_alu * 1e6, 3), "hbm": round(t_hbm * 1e6, 3)},
                 other[0]: other[1]}
+    np_work = FLOP_EQ_PER_UPDATE_NO_PACKED * w.tuples
+    np_achieved = np_work / (avg_ms * 1e-3) / 1e12
+    roofline["alu_no_packed_fp32"] = {
+        "achieved": round(np_achieved, 3), "peak": ALU_PEAK_NO_PACKED_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(np_achieved / ALU_PEAK_NO_PACKED_TFLOPS, 4),
+        "floor_us": round(np_work / (ALU_PEAK_NO_PACKED_TFLOPS * 1e12) * 1e6, 3),
+        "work": (f"{FLOP_EQ_PER_UPDATE_NO_PACKED} flop-equivalents per update (4 wave64 VALU "
+                 "instructions at 4 clocks + 1 v_exp_f32 at 8 clocks) x "
+                 f"{w.tuples} updates per launch"),
+        "basis": "the build disables packed fp32 (v_pk_fma_f32), which the 157.3 TFLOP/s "
+                 "peak needs; this is the peak of the instructions the kernel can issue"}
 
     result = {
         "metric": ("scan GB/s & % HBM peak (1 MI355X), b4 d2048 N16 L2048 bf16"

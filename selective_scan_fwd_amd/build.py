@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libssmscan.so")
+# The VALU throughput probes bench.py --alu-probe runs; a library of their own.
+PROBE_SOURCE = os.path.join(PKG, "probes", "alu_probe.hip")
+PROBE_LIB_PATH = os.path.join(PKG, "libssmprobe.so")
 SOURCES = ["scan_kernels.hip", "scan_short.hip", "scan_bwd.hip", "ssd_kernels.hip", "scan_api.cpp",
            "ssd_api.cpp"]
 ARCH = "gfx950"
@@ -33,19 +36,24 @@ def compile_flags() -> list:
             "-fvisibility=hidden", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    fd, tmp = tempfile.mkstemp(prefix="libssmscan.", suffix=".so.tmp", dir=PKG)
+def _link(sources, target, verbose):
+    fd, tmp = tempfile.mkstemp(prefix=os.path.basename(target) + ".", suffix=".tmp", dir=PKG)
     os.close(fd)
-    cmd = [hipcc(), *compile_flags(), "-shared", "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+    cmd = [hipcc(), *compile_flags(), "-shared", "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, cwd=PKG, capture_output=True, text=True)
     if r.returncode != 0:
         os.unlink(tmp)
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, target)
+    return target
+
+
+def build(verbose: bool = False) -> str:
+    """Build libssmscan.so (the scan library) and libssmprobe.so (the VALU probes)."""
+    _link([PROBE_SOURCE], PROBE_LIB_PATH, verbose)
+    return _link([os.path.join(CSRC, s) for s in SOURCES], LIB_PATH, verbose)
 
 
 if __name__ == "__main__":

@@ -180,3 +180,20 @@ def test_ssd_empty_is_a_noop():
     assert ssd_call(batch=0) == ssm.SSM_OK
     assert ssd_call(nheads=0, A=None) == ssm.SSM_OK
     assert ssd_call(seqlen=0, flags=BF | ssm.SSM_INITIAL_STATE, final_state=FIN) == ssm.SSM_OK
+
+
+def test_probe_library_exports_and_validates():
+    """libssmprobe.so (the VALU probes of bench.py --alu-probe) is built beside the scan
+    library, exports its two calls, and refuses bad arguments before any HIP call."""
+    import ctypes
+
+    from selective_scan_fwd_amd.build import PROBE_LIB_PATH
+    lib = ctypes.CDLL(PROBE_LIB_PATH)
+    lib.ssm_probe_alu.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.ssm_probe_ops_per_launch.argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.ssm_probe_ops_per_launch.restype = ctypes.c_int64
+    assert lib.ssm_probe_ops_per_launch(4, 200) == 4 * 256 * 200 * 32 * 8
+    assert lib.ssm_probe_alu(2, 4, 1, 16, None) == -1       # unknown kind
+    assert lib.ssm_probe_alu(0, 0, 1, 16, None) == -1       # no blocks
+    assert lib.ssm_probe_alu(0, 4, 1, None, None) == -1     # no output
