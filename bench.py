@@ -357,14 +357,22 @@ def cpu_baseline_bwd(w, inp, budget_s: float):
 def ssd_mfma_flops(w) -> int:
     """Matrix-core flops one ssm_ssd_fwd call issues (16x16x32 bf16 products of 16384
     flops). A workgroup of 32 channels runs 2 x ns waves (ns = 4 state splits at 128 states,
-    else 2); per wave and 64-step block: the carried-state product (4 step tiles x its
-    32-state k-blocks x 2 halves), the block-diagonal product (2 per output tile) and the
-    state update (its 16-state tiles x 2 k-blocks x 2 halves). The prep kernel adds G
-    (16 tiles x dstate/32 k-blocks per batch row and block)."""
+    else 2). Per wave and 64-step block, up to 128 states (ssd_chunk_kernel, own = 4 / ns
+    output tiles per wave): the carried-state product (own x dstate/32 k-blocks x 2 halves),
+    the block-diagonal product in the separable form (own x 2 k-blocks x 2 halves; every
+    block of the benchmark workloads takes that form) and the state update (2 tiles x 2
+    k-blocks x 2 halves). At 256 states (ssd_fwd_kernel): the carried-state product over
+    the wave's states for all 4 step tiles, the block matrix product (2 per output tile)
+    and the state update. The prep kernel adds G (16 tiles x dstate/32 k-blocks per batch
+    row and block)."""
     blocks = -(-w.seqlen // 64)
     ns = 4 if w.dstate == 128 else 2
-    nw = w.dstate // ns
-    per_wave = 4 * (nw // 32) * 2 + 2 * (4 // ns) + (nw // 16) * 2 * 2
+    if w.dstate <= 128:
+        own = 4 // ns
+        per_wave = own * (w.dstate // 32) * 2 + own * 4 + 8
+    else:
+        nw = w.dstate // ns
+        per_wave = 4 * (nw // 32) * 2 + 2 * (4 // ns) + (nw // 16) * 2 * 2
     waves = 2 * ns * w.batch * w.nheads * (-(-w.headdim // 32))
     prep = 16 * (w.dstate // 32) * w.batch
     return 16384 * blocks * (per_wave * waves + prep)
@@ -381,7 +389,7 @@ def bench_ssd(args, w, torch, ssm, dev) -> int:
                                                         "dt_bias", "h0")}
     set_bytes = w.algorithmic_bytes()
     nsets = args.sets or max(2, math.ceil(2 * INFINITY_CACHE_BYTES / set_bytes))
-    ws_bytes = ssm.ssm_ssd_workspace_bytes(w.batch, w.dstate, w.seqlen)
+    ws_bytes = ssm.ssm_ssd_workspace_bytes(w.batch, w.nheads, w.dstate, w.seqlen)
     sets = []
     for i in range(nsets):
         s = {k: (v if (i == 0 or v is None) else v.clone()) for k, v in base.items()}
@@ -419,7 +427,8 @@ def bench_ssd(args, w, torch, ssm, dev) -> int:
            "work": f"{set_bytes} algorithmic bytes per call"}
     main_, other = (("mfma", mfma), ("hbm", hbm)) if t_mfma >= t_hbm else (("hbm", hbm), ("mfma", mfma))
     roofline = {"bound": main_[0], **main_[1], "traffic": load_traffic(args.workload, "ssd"),
-                "kernel": "ssd_prep_kernel + ssd_fwd_kernel (one call)",
+                "kernel": ("ssd_prep_kernel + ssd_chunk_kernel (one call)" if w.dstate <= 128
+                           else "ssd_prep_kernel + ssd_fwd_kernel (one call)"),
                 "kernel_hash": kernel_hash("ssd"),
                 "floor_us": {"mfma": round(t_mfma * 1e6, 3), "hbm": round(t_hbm * 1e6, 3)},
                 other[0]: other[1]}

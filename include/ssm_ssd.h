@@ -19,10 +19,11 @@
  * lower-triangular matrix per head; section 5.2, blocks handled by matrix products and a
  * scan between blocks) and ybb.press section 4.4 / section 8.1 (matrix units for the
  * large-state case). In 64-step blocks the kernels form G = C^T B once per (batch row,
- * block) and, per head, the decayed block matrix, the block-end state and the carried
- * state's contribution as bf16 MFMA products with fp32 accumulation; the state itself is
- * carried in fp32 (its block update uses a two-term bf16 split of its right operand, so it
- * keeps fp32-level accuracy).
+ * block) and, per head, the block-diagonal part, the block-end state and the carried
+ * state's contribution as bf16 MFMA products with fp32 accumulation (the decay between
+ * two steps of a block factored through the block's midpoint where its range allows, the
+ * decayed block matrix otherwise); the state itself is carried in fp32 (every fp32 value
+ * that enters a product is split into two bf16 terms, so it keeps fp32-level accuracy).
  *
  * Memory: device pointers owned by the caller; C-contiguous arrays:
  *   x, z, out   : [batch, nheads*headdim, seqlen]   bf16
@@ -33,7 +34,7 @@
  *   mask        : [batch, seqlen] bytes, 0 = padding step (the state is kept), as the
  *                 padding mask of mhpq.cn/news/1057127 (section 4)
  *   final_state : [batch, nheads*headdim, dstate]   fp32 (in/out with SSM_INITIAL_STATE)
- *   workspace   : ssm_ssd_workspace_bytes(batch, dstate, seqlen) bytes, 256-byte aligned,
+ *   workspace   : ssm_ssd_workspace_bytes(batch, nheads, dstate, seqlen) bytes, 256-byte aligned,
  *                 scratch owned by the caller; its contents are overwritten and need not be
  *                 kept between calls. Calls that share a workspace must not overlap.
  *
@@ -55,8 +56,10 @@ extern "C" {
 #endif
 
 /* Bytes of workspace ssm_ssd_fwd needs: per (batch row, 64-step block) 64x64 bf16 for G
- * and 64 x dstate bf16 for C^T. 0 for empty problems; -1 for negative sizes. */
-SSM_API int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t dstate, int64_t seqlen);
+ * and 64 x dstate bf16 for C^T, and per (batch row, head, block) 1 KB of per-step factors
+ * (4 x 64 fp32). 0 for empty problems; -1 for negative sizes or a size past int64. */
+SSM_API int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t nheads, int64_t dstate,
+                                        int64_t seqlen);
 
 /*
  * ssm_ssd_fwd -- the Mamba-2 forward described above.

@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
     L.ssm_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
                                vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
     L.ssm_scan_bwd.restype = ctypes.c_int
-    L.ssm_ssd_workspace_bytes.argtypes = [i64, i64, i64]
+    L.ssm_ssd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.ssm_ssd_workspace_bytes.restype = i64
     L.ssm_ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
                               i64, i64, i64, i64, i64, i64, vp]
@@ -131,8 +131,8 @@ def ssm_scan_debug_wave_combine(a, b, a_out, b_out, groups, stream) -> int:
     return lib().ssm_scan_debug_wave_combine(a, b, a_out, b_out, groups, stream)
 
 
-def ssm_ssd_workspace_bytes(batch, dstate, seqlen) -> int:
-    return lib().ssm_ssd_workspace_bytes(batch, dstate, seqlen)
+def ssm_ssd_workspace_bytes(batch, nheads, dstate, seqlen) -> int:
+    return lib().ssm_ssd_workspace_bytes(batch, nheads, dstate, seqlen)
 
 
 def ssm_ssd_fwd(x, dt, A, B, C, D, z, dt_bias, mask, flags, out, final_state, workspace,
@@ -366,7 +366,7 @@ def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = False,
             final_state.copy_(h0)
     elif final_state is None and return_final_state:
         final_state = torch.empty((batch, dim, dstate), device=x.device, dtype=torch.float32)
-    need = ssm_ssd_workspace_bytes(batch, max(dstate, 0), seqlen)
+    need = ssm_ssd_workspace_bytes(batch, nheads, max(dstate, 0), seqlen)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), device=x.device, dtype=torch.uint8)
     status = ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),

@@ -21,13 +21,19 @@ int64_t nblocks_of(int64_t seqlen) { return (seqlen + ssm::kSsdBlock - 1) / ssm:
 
 extern "C" {
 
-int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t dstate, int64_t seqlen) {
-  if (batch < 0 || dstate < 0 || seqlen < 0) return -1;
-  int64_t per_block, blocks, total;
+int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t nheads, int64_t dstate,
+                                int64_t seqlen) {
+  if (batch < 0 || nheads < 0 || dstate < 0 || seqlen < 0) return -1;
+  int64_t per_block, blocks, shared, head_blocks, steps, total;
   const int64_t q = ssm::kSsdBlock;
+  // per (batch row, block): G (q x q bf16) and C^T (q x dstate bf16); per (batch row, head,
+  // block): the step record, 4 x q fp32
   if (!mul_ok(dstate, 2 * q, &per_block) || !mul_ok(batch, nblocks_of(seqlen), &blocks) ||
-      !mul_ok(blocks, q * q * 2 + per_block, &total))
+      !mul_ok(blocks, q * q * 2 + per_block, &shared) ||
+      !mul_ok(blocks, nheads, &head_blocks) || !mul_ok(head_blocks, 4 * q * 4, &steps) ||
+      shared > INT64_MAX - steps)
     return -1;
+  total = shared + steps;
   return total;
 }
 
@@ -55,11 +61,12 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
   if (row_elems * 2 >= (int64_t(1) << 31) || bc_row * 2 >= (int64_t(1) << 31) ||
       batch > 65535 || nheads > 65535 || seqlen > kInt32Max)
     return SSM_ERR_UNSUPPORTED;
-  need = ssm_ssd_workspace_bytes(batch, dstate, seqlen);
+  need = ssm_ssd_workspace_bytes(batch, nheads, dstate, seqlen);
   if (need < 0) return SSM_ERR_UNSUPPORTED;
-  // Both kernels run one-dimensional grids: (batch x blocks) and (batch x heads x groups of
-  // 32 channels) workgroups.
-  if (batch * nblocks_of(seqlen) > kInt32Max || batch * nheads * ((headdim + 31) / 32) > kInt32Max)
+  // The kernels run one-dimensional grids: batch x blocks plus (batch x heads x blocks) / 4
+  // workgroups, and batch x heads x groups of 32 channels.
+  if (batch * nblocks_of(seqlen) + (batch * nheads * nblocks_of(seqlen) + 3) / 4 > kInt32Max ||
+      batch * nheads * ((headdim + 31) / 32) > kInt32Max)
     return SSM_ERR_UNSUPPORTED;
 
   const bool any = elems > 0;

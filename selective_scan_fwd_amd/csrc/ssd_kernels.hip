@@ -11,26 +11,35 @@
 //         + exp(cs_t) C_t . H_in                                  (the carried state)
 //   H_out = exp(cs_end) H_in + sum_s exp(cs_end - cs_s) dt_s B_s x_s^T
 //
-// Two kernels:
-//   ssd_prep_kernel, one workgroup per (batch row, 64-step block): G = C^T B of the block
-//     (MFMA over the states, stored bf16) and C^T in the lane order and swizzle the main
-//     kernel's operands use. Both depend only on the batch row; every head reuses them.
-//   ssd_fwd_kernel, one workgroup per (batch row, head, 32 channels), blocks in order:
-//     the decayed block matrix M = G o exp(cs_t - cs_s) o dt_s (bf16, LDS), then per wave
-//     Y = exp(cs_t) C^T H_in + M x (MFMA), the D skip and gate, and
-//     H_out = exp(cs_end) H_in + B (w o x) (MFMA). Wherever the fp32 state or a value
+// Where a block's decay span -cs_end is moderate, exp(cs_t - cs_s) factors as
+// exp(cs_t - ref) exp(ref - cs_s) (ref = cs_end / 2), and the block-diagonal part becomes
+// exp(cs_t - ref) ((G o L) xs) with xs_s = exp(ref - cs_s) dt_s x_s and L the causal mask:
+// no per-head block matrix is formed, and xs is the operand the state update needs too.
+// Blocks of larger span use M = G o exp(cs_t - cs_s) o dt_s directly.
+//
+// Two launches:
+//   ssd_prep_kernel: per (batch row, 64-step block), G o L with G = C^T B (MFMA over the
+//     states, stored bf16) and C^T in the lane order and swizzle the block kernels' operands
+//     use, shared by every head; and per (batch row, head, block), a record of the step
+//     sizes, their running sums and the per-step factors (ssd_step_record).
+//   ssd_chunk_kernel (up to 128 states) or ssd_fwd_kernel (256 states), one workgroup per
+//     (batch row, head, 32 channels), blocks in order: per wave y = the carried state read
+//     through C plus the block-diagonal product (MFMA), the D skip and gate, and the state
+//     update H_out = exp(cs_end) H_in + B (w o x) (MFMA). Wherever the fp32 state or a value
 //     that feeds it is an MFMA operand (H_in in the carried-state product, w o x in the
 //     update), it enters as two bf16 halves, hi + lo, which keeps fp32-level accuracy.
 //
-// Wave layout of ssd_fwd_kernel: 2 channel blocks of 16 x kNS splits of the states (kNS = 4
-// for 128 states: 8 waves, two per SIMD; 2 otherwise). A wave holds its slice of H as MFMA
-// accumulators; the waves of a channel block split the carried-state product over the
-// states and sum the partial outputs through LDS.
+// Wave layout: 2 channel blocks of 16 x kNS splits of the states (kNS = 4 for 128 states:
+// 8 waves, two per SIMD; 2 otherwise). A wave holds its slice of H as MFMA accumulators.
+// ssd_chunk_kernel hands the slices to every wave through LDS once per block, so each wave
+// forms whole output tiles and a block needs one barrier; ssd_fwd_kernel (whose two B and
+// C^T stages alone fill 128 KB of LDS at 256 states) splits the carried-state product over
+// the states and sums partial outputs through LDS instead.
 //
 // Data movement: the next block's B and C^T (and, up to 128 states, G, x and z) travel by
-// buffer-to-LDS DMA into a second stage while the current block computes, issued in three
-// groups spread over the block, so that the CU's vector memory path (about 64 bytes per
-// clock) works in the background instead of stalling every wave at one point.
+// buffer-to-LDS DMA into a second stage while the current block computes, so that the
+// CU's vector memory path works in the background instead of stalling every wave at one
+// point.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 lane layout (checked on the device): lane l, r = l % 16,
 // g = l / 16: A operand row r, k = 8g..8g+7; B operand column r, the same k; result rows
@@ -57,10 +66,21 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kQ = kSsdBlock;          // steps per block
 constexpr int kMPitch = kQ + 8;        // bf16 per row of the block matrix in LDS
 constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every buffer: loads read 0
+// Largest decay span -cs_end of a block (natural log units) that takes the separable form:
+// its two factors then stay within exp(+-60).
+constexpr float kSepSpan = 120.0f;
 
 __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 loads through a buffer resource (byte offsets; past the end they read 0).
+__device__ __forceinline__ float4 ld_f4(const Buf& b, uint32_t off) {
+  return __builtin_bit_cast(float4, b.load16(off));
+}
+__device__ __forceinline__ float ld_f1(const Buf& b, uint32_t off) {
+  return __uint_as_float(b.load4(off));
 }
 
 // 8 consecutive bf16 of a row (elements [row + t, row + t + 8)); elements at or past len
@@ -164,20 +184,61 @@ struct SsdParams {
   const uint8_t* mask;
   uint16_t* out;
   float* final_state;
-  uint16_t* G;       // [batch, nblocks, 64, 64] bf16
+  uint16_t* G;       // [batch, nblocks, 64, 64] bf16, G o L, rows swizzled
   uint16_t* CTp;     // [batch, nblocks, 64, dstate], states in operand order, swizzled
+  float* steps;      // [batch, nheads, nblocks, 4, 64]: w, e, cs, dt of every step
   int nheads, headdim, seqlen, nblocks;
   int softplus, initial_state;
 };
 
+// ---------------------------------------------------------------- step sizes of every head
+
+// One wave per record (batch row, head, block), lane = step: the step size dt_t (bias, softplus,
+// zero at padding and past the end), its running sum cs_t over the block (a_r = dt_r A),
+// and the per-step factors the block kernel applies, written as one 1 KB record
+// [w | e | cs | dt] of 64 fp32 each. With ref = cs_end / 2 when the block's decay span
+// -cs_end is at most kSepSpan (the separable form) and ref = cs_end otherwise:
+//   w_s = exp(ref - cs_s) dt_s        (scales x_s for the state update and the block product)
+//   e_t = exp(cs_t - ref) (separable) or exp(cs_t)      (the output factor)
+__device__ __forceinline__ void ssd_step_record(const SsdParams& p, int64_t rec) {
+  const int l = threadIdx.x & 63, L = p.seqlen;
+  const int c = int(rec % p.nblocks);
+  const int h = int((rec / p.nblocks) % p.nheads);
+  const int64_t b = rec / (int64_t(p.nblocks) * p.nheads);
+  const int t = c * kQ + l;
+  const bool in = t < L;
+  const uint16_t* dtrow = p.dt + (b * p.nheads + h) * L;
+  float s = in ? bf16_lo(dtrow[t]) : 0.0f;
+  s += p.dt_bias ? p.dt_bias[h] : 0.0f;
+  s = p.softplus ? softplus_f(s) : s;
+  const bool live = in && (p.mask == nullptr || p.mask[b * L + t] != 0);
+  s = live ? s : 0.0f;
+  const float cs = wave_prefix_sum(s * p.A[h]);
+  const float cs_end = readlane(cs, 63);
+  const bool sep = cs_end >= -kSepSpan;
+  const float ref = sep ? 0.5f * cs_end : cs_end;
+  float* out = p.steps + rec * (4 * kQ);
+  out[l] = exp2_hw((ref - cs) * kLog2e) * s;
+  out[kQ + l] = exp2_hw((cs - (sep ? ref : 0.0f)) * kLog2e);
+  out[2 * kQ + l] = cs;
+  out[3 * kQ + l] = s;
+}
+
 // ---------------------------------------------------------------- prep: G and C^T
 
+// Workgroups [0, n_prep) take one (batch row, block) each; the ones after them take four
+// step records each (one per wave), so the two kinds of work share one launch.
 template <int N, bool kVec>
-__global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
+__global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p, int n_prep, int64_t records) {
   constexpr int kPitch = N + 8;  // bf16 per LDS row
   __shared__ __attribute__((aligned(16))) uint16_t ct[kQ][kPitch];  // C^T of the block
   __shared__ __attribute__((aligned(16))) uint16_t bt[kQ][kPitch];  // B^T of the block
-  const int logical = xcd_order(blockIdx.x, gridDim.x);  // one batch row's blocks together
+  if (int(blockIdx.x) >= n_prep) {
+    const int64_t rec = int64_t(int(blockIdx.x) - n_prep) * 4 + (threadIdx.x >> 6);
+    if (rec < records) ssd_step_record(p, rec);
+    return;
+  }
+  const int logical = xcd_order(blockIdx.x, n_prep);  // one batch row's blocks together
   const int c = logical % p.nblocks, b = logical / p.nblocks, L = p.seqlen, t0 = c * kQ;
   const uint32_t bc_bytes = uint32_t(N) * uint32_t(L) * 2u;
   const Buf cbuf(p.C + size_t(b) * N * L, bc_bytes), bbuf(p.B + size_t(b) * N * L, bc_bytes);
@@ -199,7 +260,8 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   __syncthreads();
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g = l >> 4;
-  // G[t][s] = sum_n C[n][t] B[n][s]: wave w takes rows 16w..16w+15 (bf16, row-major).
+  // G[t][s] = sum_n C[n][t] B[n][s] for s <= t, 0 above the diagonal: wave w takes rows
+  // 16w..16w+15 (bf16, rows of 8 words, word q of row t in slot q ^ row_swizzle(t)).
   uint16_t* G = p.G + (size_t(b) * p.nblocks + c) * (kQ * kQ);
 #pragma unroll
   for (int sj = 0; sj < kQ / 16; ++sj) {
@@ -211,8 +273,11 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
       acc = mfma16(a, bv, acc);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      G[(16 * w + 4 * g + i) * kQ + 16 * sj + r] = uint16_t(pack_bf16x2(acc[i], 0.0f));
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * g + i, sc = 16 * sj + r;
+      const float v = sc <= t ? acc[i] : 0.0f;  // causal: zero above the diagonal
+      G[t * kQ + 8 * ((sc >> 3) ^ row_swizzle(t)) + (sc & 7)] = uint16_t(pack_bf16x2(v, 0.0f));
+    }
   }
 
   // C^T with the states of each 32-block in operand order (position 8g' + j holds state
@@ -228,11 +293,13 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   }
 }
 
-// ---------------------------------------------------------------- the block scan
+// ---------------------------------------------------------------- the block scan, 256 states
 
-// States split across waves: 128 states in quarters (8 waves, two per SIMD); 64 states in
-// halves (a quarter would be 16, below the 32-deep MFMA); 256 states in halves (its two
-// B and C^T stages alone fill 128 KB of LDS).
+// The launcher runs ssd_fwd_kernel for 256 states only (ssd_chunk_kernel below takes 64 and
+// 128); its layout still covers every size. States split across waves: 128 states in
+// quarters (8 waves, two per SIMD); 64 states in halves (a quarter would be 16, below the
+// 32-deep MFMA); 256 states in halves (its two B and C^T stages alone fill 128 KB of LDS).
+// It computes its step sizes itself rather than reading the step records.
 template <int N>
 struct StateSplit {
   static constexpr int kNS = N == 128 ? 4 : 2;
@@ -391,10 +458,12 @@ __global__ __launch_bounds__(128 * kNS) void ssd_fwd_kernel(SsdParams p) {
     ld.live = __builtin_amdgcn_raw_buffer_load_b8(mbuf.r, t0 + l < L ? uint32_t(t0 + l) : kOob, 0,
                                                   0);  // reads 0 without a mask
     if constexpr (!kStageAll) {
-      const uint32_t goff =
-          c < p.nblocks ? 2u * (uint32_t(c) * (kQ * kQ) + uint32_t(mt) * kQ + uint32_t(ms0)) : kOob;
+      const uint32_t grow = 2u * (uint32_t(c) * (kQ * kQ) + uint32_t(mt) * kQ);
 #pragma unroll
-      for (int q = 0; q < kEPT / 8; ++q) ld.g[q] = gbuf.load16(c < p.nblocks ? goff + 16u * q : kOob);
+      for (int q = 0; q < kEPT / 8; ++q)
+        ld.g[q] = gbuf.load16(c < p.nblocks
+                                  ? grow + 16u * uint32_t((ms0 / 8 + q) ^ row_swizzle(mt))
+                                  : kOob);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) ld.xo[kb] = load8<kVec>(xbuf, xrow, t0 + 32 * kb + 8 * g, L);
       const int tz = p.z ? L : 0;
@@ -498,7 +567,7 @@ __global__ __launch_bounds__(128 * kNS) void ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
       for (int q = 0; q < kEPT / 8; ++q) {
         if constexpr (kStageAll)
-          gw[q] = sGb[mt * 8 + ms0 / 8 + q];
+          gw[q] = sGb[mt * 8 + ((ms0 / 8 + q) ^ row_swizzle(mt))];
         else
           gw[q] = cur.g[q];
       }
@@ -534,14 +603,30 @@ __global__ __launch_bounds__(128 * kNS) void ssd_fwd_kernel(SsdParams p) {
     // next block's start can leave exactly those stores outstanding.
     issue_xz(Next(), c + 1, nxt);
 
-    // x operands of this wave's channels (steps 32kb + 8g .. +7).
-    uint4 xo[2];
+    // x operands of this wave's channels (steps 32kb + 8g .. +7), and x scaled per step by
+    // w_s = exp(cs_end - cs_s) dt_s, split hi + lo.
+    uint4 xo[2], xh[2], xl[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (kStageAll)
         xo[kb] = sXb[xr * 8 + ((4 * kb + g) ^ row_swizzle(xr))];
       else
         xo[kb] = cur.xo[kb];
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_wdt[buf][32 * kb + 8 * g]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_wdt[buf][32 * kb + 8 * g + 4]);
+      const uint4 xw = xo[kb];
+      const float xv[8] = {bf16_lo(xw.x) * w0[0], bf16_hi(xw.x) * w0[1],
+                           bf16_lo(xw.y) * w0[2], bf16_hi(xw.y) * w0[3],
+                           bf16_lo(xw.z) * w1[0], bf16_hi(xw.z) * w1[1],
+                           bf16_lo(xw.w) * w1[2], bf16_hi(xw.w) * w1[3]};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hi[q] = pack_bf16x2(xv[2 * q], xv[2 * q + 1]);
+        lo[q] = pack_bf16x2(xv[2 * q] - bf16_lo(hi[q]), xv[2 * q + 1] - bf16_hi(hi[q]));
+      }
+      xh[kb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      xl[kb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
 
 #pragma unroll
@@ -550,13 +635,13 @@ __global__ __launch_bounds__(128 * kNS) void ssd_fwd_kernel(SsdParams p) {
       f32x4 Yo = sY[pb][i][l];
 #pragma unroll
       for (int q = 1; q < kNS; ++q) Yo += sY[pb + 2 * q][i][l];
-      // exp(cs_t) on the carried part, then the block-diagonal product on top.
+      // exp(cs_t) on the carried part, then the block-diagonal product on top. Both 32-step
+      // halves, also for tiles 0 and 1 whose second half of M is zero: a branch here would
+      // cost more than the product (the compiler then also waits for the DMA in flight
+      // before the LDS read inside it).
       const f32x4 csr = *reinterpret_cast<const f32x4*>(&s_cs[buf][16 * i + 4 * g]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) Yo[q] *= exp2_hw(csr[q] * kLog2e);
-      // Both 32-step halves, also for tiles 0 and 1 whose second half of M is zero: a
-      // branch here would cost more than the product (the compiler then also waits for
-      // the DMA in flight before the LDS read inside it).
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const uint4 a = *reinterpret_cast<const uint4*>(&sM[16 * i + r][32 * kb + 8 * g]);
@@ -583,35 +668,22 @@ __global__ __launch_bounds__(128 * kNS) void ssd_fwd_kernel(SsdParams p) {
       store4<kVec>(obuf, xrow, t0 + 16 * i + 4 * g, L, wave_on, y);
     }
 
-    // State: H <- exp(cs_end) H + B (wdt o x), x scaled per step and split hi + lo.
-    const float dec = exp2_hw(cs_end * kLog2e);
+    // State: H <- exp(cs_end) H + B (w o x).
+    {
+      const float dec = exp2_hw(cs_end * kLog2e);
 #pragma unroll
-    for (int j = 0; j < kNT; ++j)
+      for (int j = 0; j < kNT; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) H[j][q] *= dec;
+        for (int q = 0; q < 4; ++q) H[j][q] *= dec;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_wdt[buf][32 * kb + 8 * g]);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_wdt[buf][32 * kb + 8 * g + 4]);
-      const uint4 xw = xo[kb];
-      const float xv[8] = {bf16_lo(xw.x) * w0[0], bf16_hi(xw.x) * w0[1],
-                           bf16_lo(xw.y) * w0[2], bf16_hi(xw.y) * w0[3],
-                           bf16_lo(xw.z) * w1[0], bf16_hi(xw.z) * w1[1],
-                           bf16_lo(xw.w) * w1[2], bf16_hi(xw.w) * w1[3]};
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        hi[q] = pack_bf16x2(xv[2 * q], xv[2 * q + 1]);
-        lo[q] = pack_bf16x2(xv[2 * q] - bf16_lo(hi[q]), xv[2 * q + 1] - bf16_hi(hi[q]));
-      }
-      const uint4 xh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      const uint4 xl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
         const int n = nq * kNW + 16 * j + r;
         const uint4 a = sBb[n * 8 + ((4 * kb + g) ^ row_swizzle(n))];
-        H[j] = mfma16(a, xh, H[j]);
-        H[j] = mfma16(a, xl, H[j]);
+        H[j] = mfma16(a, xh[kb], H[j]);
+        H[j] = mfma16(a, xl[kb], H[j]);
       }
     }
   };
@@ -633,13 +705,347 @@ __global__ __launch_bounds__(128 * kNS) void ssd_fwd_kernel(SsdParams p) {
   }
 }
 
+// ---------------------------------------------------------------- the block scan, one barrier
+
+// Up to 128 states. Wave layout as above: 2 channel blocks of 16 x kNS state splits of 32
+// states; a wave keeps its 32 x 16 slice of H as MFMA accumulators. At the end of every
+// block each wave writes its slice, split hi + lo in the operand order of the carried-state
+// product, to LDS; the barrier at the next block's start publishes it with the staged B,
+// C^T, G, x and z of that block, and every wave then forms its own output tiles over all
+// the states. One barrier per block, and no reduction of partial outputs between waves.
+template <int N>
+struct ChunkLayout {
+  static constexpr int kNS = N == 128 ? 4 : 2;   // state splits of 32
+  static constexpr int kWaves = 2 * kNS;
+  static constexpr int kKB = N / 32;              // 32-state k-blocks of the whole state
+  static constexpr int kOwn = 4 / kNS;            // 16-step output tiles per wave
+  static constexpr int kBInstr = N / 8 / kWaves;  // 1 KB copies of B (and of C^T) per wave
+  static constexpr int kGInstr = 8 / kWaves;      // of G
+  static constexpr int kXZInstr = 8 / kWaves;     // of x and z (4 copies each)
+};
+
+template <int N, bool kVec>
+struct ChunkLoads {
+  using CL = ChunkLayout<N>;
+  float4 w[4];            // w_s, s = 32 kb + 8 g + 4 k .. + 3  (index 2 kb + k)
+  float4 e[CL::kOwn];     // e_t at this lane's output rows
+  float cse;              // cs_end of the block
+  uint4 bst[kVec ? 1 : CL::kBInstr];   // element-wise path: B and x/z words for the stages
+  uint4 xst[kVec ? 1 : CL::kXZInstr];
+};
+
+template <int N, bool kVec>
+__global__ __launch_bounds__(128 * ChunkLayout<N>::kNS) void ssd_chunk_kernel(SsdParams p) {
+  using CL = ChunkLayout<N>;
+  using LL = ChunkLoads<N, kVec>;
+  constexpr int kNS = CL::kNS, kWaves = CL::kWaves, kKB = CL::kKB, kOwn = CL::kOwn;
+  constexpr int kBInstr = CL::kBInstr, kGInstr = CL::kGInstr, kXZInstr = CL::kXZInstr;
+  constexpr int kRowWords = N / 8;                 // 16-byte words per C^T row
+  constexpr int kXW = 32 * 8;                      // words of the x (or z) stage
+  constexpr int kStores = kOwn * (kVec ? 1 : 4);
+  static_assert(kBInstr >= 1 && kGInstr >= 1 && kXZInstr >= 1, "unsupported split");
+  // LDS: two stages, each array of each stage its own variable (see ssd_fwd_kernel).
+  __shared__ __attribute__((aligned(16))) uint4 sB0[N * 8], sB1[N * 8];
+  __shared__ __attribute__((aligned(16))) uint4 sCT0[kQ * kRowWords], sCT1[kQ * kRowWords];
+  __shared__ __attribute__((aligned(16))) uint4 sG0[kQ * 8], sG1[kQ * 8];
+  __shared__ __attribute__((aligned(16))) uint4 sXZ0[2 * kXW], sXZ1[2 * kXW];
+  __shared__ __attribute__((aligned(16))) uint4 sH0[2][kNS][2][64], sH1[2][kNS][2][64];
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int pb = w & 1, nq = w >> 1;       // channel block, state split
+  const int pgroups = (p.headdim + 31) / 32;
+  const int logical = xcd_order(blockIdx.x, gridDim.x);
+  const int pg = logical % pgroups, h = (logical / pgroups) % p.nheads;
+  const int b = logical / (pgroups * p.nheads);
+  const int P = p.headdim, L = p.seqlen, dim = p.nheads * P;
+  const int p0 = pg * 32 + pb * 16;
+  const bool wave_on = p0 < P;
+  const int d = h * P + p0 + r;
+  const int xr = pb * 16 + r;
+
+  const uint32_t row_bytes = uint32_t(dim) * uint32_t(L) * 2u;
+  const Buf xbuf(p.x + size_t(b) * dim * L, row_bytes);
+  const Buf zbuf(p.z ? p.z + size_t(b) * dim * L : p.x, p.z ? row_bytes : 0u);
+  const Buf obuf(p.out + size_t(b) * dim * L, row_bytes);
+  const Buf bbuf(p.B + size_t(b) * N * L, uint32_t(N) * uint32_t(L) * 2u);
+  const Buf ctbuf(p.CTp + size_t(b) * p.nblocks * (kQ * N), uint32_t(p.nblocks) * (kQ * N * 2));
+  const Buf gbuf(p.G + size_t(b) * p.nblocks * (kQ * kQ), uint32_t(p.nblocks) * (kQ * kQ * 2));
+  const Buf sbuf(p.steps + (size_t(b) * p.nheads + h) * p.nblocks * (4 * kQ),
+                 uint32_t(p.nblocks) * (4 * kQ * 4));
+  const uint32_t xrow = uint32_t(d) * uint32_t(L);
+  const uint32_t xrow0 = uint32_t(h * P + pg * 32) * uint32_t(L);
+  const int xvalid = P - pg * 32;
+  const float D_d = (p.D && wave_on) ? p.D[d] : 0.0f;
+
+  // This wave's slice of H: tile j holds states 32 nq + 16 j + 4 g + i of channel r.
+  f32x4 H[2];
+  float* fs = p.final_state ? p.final_state + (size_t(b) * dim + d) * N : nullptr;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    H[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.initial_state && wave_on)
+      H[j] = *reinterpret_cast<const f32x4*>(fs + 32 * nq + 16 * j + 4 * g);
+  }
+  // H as the B operand of the carried-state product, in two bf16 halves: lane (r, g) holds
+  // k = 8 g .. 8 g + 7 of this wave's 32-state block = states {4g..4g+3, 16+4g..16+4g+3}.
+  auto write_slice = [&](auto tag) {
+    auto& sH = decltype(tag)::value == 0 ? sH0 : sH1;
+    uint32_t whi[4], wlo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4& a = H[q >> 1];
+      const float v0 = a[2 * (q & 1)], v1 = a[2 * (q & 1) + 1];
+      whi[q] = pack_bf16x2(v0, v1);
+      wlo[q] = pack_bf16x2(v0 - bf16_lo(whi[q]), v1 - bf16_hi(whi[q]));
+    }
+    sH[pb][nq][0][l] = make_uint4(whi[0], whi[1], whi[2], whi[3]);
+    sH[pb][nq][1][l] = make_uint4(wlo[0], wlo[1], wlo[2], wlo[3]);
+  };
+
+  auto row_copy = [&](const Buf& src, uint32_t row0, int k, int c, uint4* dst, uint4& reg,
+                      int valid_rows) {
+    const int n = 8 * k + (l >> 3);
+    const int t = c * kQ + 8 * ((l & 7) ^ row_swizzle(n));
+    if constexpr (kVec) {
+      const uint32_t off =
+          (t < L && n < valid_rows) ? 2u * (row0 + uint32_t(n) * uint32_t(L) + uint32_t(t)) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_void_t*)&dst[k * 64], 16, off, 0, 0, 0);
+    } else {
+      reg = load8<false>(src, row0 + uint32_t(n) * uint32_t(L), t, n < valid_rows ? L : 0);
+    }
+  };
+  auto lin_copy = [&](const Buf& src, uint32_t block_bytes, int k, int c, uint4* dst) {
+    const uint32_t off = c < p.nblocks
+                             ? uint32_t(c) * block_bytes + uint32_t(k) * 1024u + uint32_t(l) * 16u
+                             : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.r, (lds_void_t*)&dst[k * 64], 16, off, 0, 0, 0);
+  };
+  // Every copy of block c into stage `tag`, and this lane's step factors of block c.
+  auto issue = [&](auto tag, int c, LL& ld) {
+    constexpr int st = decltype(tag)::value;
+    uint4* sBs = st == 0 ? sB0 : sB1;
+    uint4* sCTs = st == 0 ? sCT0 : sCT1;
+    uint4* sGs = st == 0 ? sG0 : sG1;
+    uint4* sXZs = st == 0 ? sXZ0 : sXZ1;
+#pragma unroll
+    for (int k = 0; k < kBInstr; ++k) row_copy(bbuf, 0u, w * kBInstr + k, c, sBs, ld.bst[k], N);
+#pragma unroll
+    for (int k = 0; k < kBInstr; ++k) lin_copy(ctbuf, kQ * N * 2, w * kBInstr + k, c, sCTs);
+#pragma unroll
+    for (int k = 0; k < kGInstr; ++k) lin_copy(gbuf, kQ * kQ * 2, w * kGInstr + k, c, sGs);
+    const int zvalid = p.z ? xvalid : 0;
+    if constexpr (kWaves == 8) {  // waves 0..3 copy x, waves 4..7 copy z (no branch)
+      const bool is_z = w >= 4;
+      row_copy(is_z ? zbuf : xbuf, xrow0, w & 3, c, sXZs + (is_z ? kXW : 0), ld.xst[0],
+               is_z ? zvalid : xvalid);
+    } else {                      // every wave copies a quarter of both
+      row_copy(xbuf, xrow0, w, c, sXZs, ld.xst[0], xvalid);
+      row_copy(zbuf, xrow0, w, c, sXZs + kXW, ld.xst[kXZInstr - 1], zvalid);
+    }
+    const uint32_t rb = c < p.nblocks ? uint32_t(c) * (4 * kQ * 4) : kOob;
+    const bool ok = c < p.nblocks;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      ld.w[q] = ld_f4(sbuf, ok ? rb + 4u * uint32_t(32 * (q >> 1) + 8 * g + 4 * (q & 1)) : kOob);
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k)
+      ld.e[k] = ld_f4(sbuf, ok ? rb + 4u * uint32_t(kQ + 16 * (nq + kNS * k) + 4 * g) : kOob);
+    ld.cse = ld_f1(sbuf, ok ? rb + 4u * uint32_t(2 * kQ + kQ - 1) : kOob);
+  };
+
+  auto block = [&](auto tag, int c, LL& cur, LL& nxt) {
+    constexpr int bb = decltype(tag)::value;  // == c & 1
+    using Next = std::integral_constant<int, bb ^ 1>;
+    const uint4* sBb = bb == 0 ? sB0 : sB1;
+    const uint4* sCTb = bb == 0 ? sCT0 : sCT1;
+    const uint4* sGb = bb == 0 ? sG0 : sG1;
+    const uint4* sXb = bb == 0 ? sXZ0 : sXZ1;
+    const uint4* sZb = sXb + kXW;
+    const auto& sHb = bb == 0 ? sH0 : sH1;
+    const int t0 = c * kQ;
+    // This block's copies have landed (the previous block's output stores may still be in
+    // flight: vector memory operations complete in issue order), then one barrier
+    // publishes them and the H slices written at the previous block's end.
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStores) : "memory");
+    if constexpr (!kVec) {
+      uint4* sBw = bb == 0 ? sB0 : sB1;
+      uint4* sXZw = bb == 0 ? sXZ0 : sXZ1;
+#pragma unroll
+      for (int k = 0; k < kBInstr; ++k) sBw[(w * kBInstr + k) * 64 + l] = cur.bst[k];
+      if constexpr (kWaves == 8) {
+        sXZw[(w >= 4 ? kXW : 0) + (w & 3) * 64 + l] = cur.xst[0];
+      } else {
+        sXZw[w * 64 + l] = cur.xst[0];
+        sXZw[kXW + w * 64 + l] = cur.xst[kXZInstr - 1];
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // The carried-state product and the B rows of this wave's states (for the state update)
+    // read this stage before the next block's copies are issued: the compiler cannot always
+    // tell such a read from the LDS the copies write, and would otherwise wait for them.
+    // Carried state over all N states: C^T H for this wave's output tiles.
+    f32x4 Yc[kOwn];
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      const int t = 16 * (nq + kNS * k) + r;
+      Yc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        const uint4 a = sCTb[t * kRowWords + ((4 * kb + g) ^ ct_swizzle<N>(t))];
+        Yc[k] = mfma16(a, sHb[pb][kb][0][l], Yc[k]);
+        Yc[k] = mfma16(a, sHb[pb][kb][1][l], Yc[k]);
+      }
+    }
+    uint4 bop[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = 32 * nq + 16 * j + r;
+        bop[kb][j] = sBb[n * 8 + ((4 * kb + g) ^ row_swizzle(n))];
+      }
+    asm volatile("" ::: "memory");
+    issue(Next(), c + 1, nxt);
+
+    const float cs_end = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(cur.cse)));
+    const bool sep = cs_end >= -kSepSpan;     // the same test as the step kernel's
+    const float ref = sep ? 0.5f * cs_end : cs_end;
+
+    // x operands of this wave's channels (steps 32 kb + 8 g .. + 7) and x scaled by w_s,
+    // split hi + lo.
+    uint4 xo[2], xh[2], xl[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      xo[kb] = sXb[xr * 8 + ((4 * kb + g) ^ row_swizzle(xr))];
+      const float4 w0 = cur.w[2 * kb], w1 = cur.w[2 * kb + 1];
+      const uint4 xw = xo[kb];
+      const float xv[8] = {bf16_lo(xw.x) * w0.x, bf16_hi(xw.x) * w0.y,
+                           bf16_lo(xw.y) * w0.z, bf16_hi(xw.y) * w0.w,
+                           bf16_lo(xw.z) * w1.x, bf16_hi(xw.z) * w1.y,
+                           bf16_lo(xw.w) * w1.z, bf16_hi(xw.w) * w1.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hi[q] = pack_bf16x2(xv[2 * q], xv[2 * q + 1]);
+        lo[q] = pack_bf16x2(xv[2 * q] - bf16_lo(hi[q]), xv[2 * q + 1] - bf16_hi(hi[q]));
+      }
+      xh[kb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      xl[kb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+
+    // Outputs: separable, y = e_t (exp(ref) C^T H + (G o L) (w o x)); otherwise
+    // y = e_t C^T H + M x with M[t][s] = G[t][s] exp(cs_t - cs_s) dt_s formed in registers,
+    // in the operand layout (lane (r, g): row t, s = 32 kb + 8 g .. + 7).
+    const float er = sep ? exp2_hw(ref * kLog2e) : 1.0f;
+#pragma unroll
+    for (int k = 0; k < kOwn; ++k) {
+      const int i = nq + kNS * k;
+      const int t = 16 * i + r;
+      f32x4 Yd = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (sep) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint4 a = sGb[t * 8 + ((4 * kb + g) ^ row_swizzle(t))];
+          Yd = mfma16(a, xh[kb], Yd);
+          Yd = mfma16(a, xl[kb], Yd);
+        }
+      } else {
+        const uint32_t rb = uint32_t(c) * (4 * kQ * 4);
+        const float cst = ld_f1(sbuf, rb + 4u * uint32_t(2 * kQ + t));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int s0 = 32 * kb + 8 * g;
+          const uint4 gw = sGb[t * 8 + ((4 * kb + g) ^ row_swizzle(t))];
+          const float4 c0 = ld_f4(sbuf, rb + 4u * uint32_t(2 * kQ + s0));
+          const float4 c1 = ld_f4(sbuf, rb + 4u * uint32_t(2 * kQ + s0 + 4));
+          const float4 d0 = ld_f4(sbuf, rb + 4u * uint32_t(3 * kQ + s0));
+          const float4 d1 = ld_f4(sbuf, rb + 4u * uint32_t(3 * kQ + s0 + 4));
+          const float cs8[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          const float dt8[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+          const uint32_t gq[4] = {gw.x, gw.y, gw.z, gw.w};
+          uint32_t m[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v[2];
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const int j = 2 * q + e2;
+              const float gv = e2 ? bf16_hi(gq[q]) : bf16_lo(gq[q]);
+              const float mv = gv * exp2_hw((cst - cs8[j]) * kLog2e) * dt8[j];
+              v[e2] = s0 + j <= t ? mv : 0.0f;
+            }
+            m[q] = pack_bf16x2(v[0], v[1]);
+          }
+          Yd = mfma16(make_uint4(m[0], m[1], m[2], m[3]), xo[kb], Yd);
+        }
+      }
+      // D skip, gate, store: rows t0 + 16 i + 4 g .. + 3 of channel d.
+      const int slot = (2 * i + (g >> 1)) ^ row_swizzle(xr);
+      const uint2 xe = reinterpret_cast<const uint2*>(&sXb[xr * 8 + slot])[g & 1];
+      const uint2 ze = reinterpret_cast<const uint2*>(&sZb[xr * 8 + slot])[g & 1];
+      const float xv[4] = {bf16_lo(xe.x), bf16_hi(xe.x), bf16_lo(xe.y), bf16_hi(xe.y)};
+      const float zv[4] = {bf16_lo(ze.x), bf16_hi(ze.x), bf16_lo(ze.y), bf16_hi(ze.y)};
+      const float ev[4] = {cur.e[k].x, cur.e[k].y, cur.e[k].z, cur.e[k].w};
+      float y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float yb = sep ? ev[q] * __builtin_fmaf(er, Yc[k][q], Yd[q])
+                             : __builtin_fmaf(ev[q], Yc[k][q], Yd[q]);
+        y[q] = __builtin_fmaf(D_d, xv[q], yb);
+        if (p.z) y[q] = gate_f(y[q], zv[q]);
+      }
+      store4<kVec>(obuf, xrow, t0 + 16 * i + 4 * g, L, wave_on, y);
+    }
+
+    // State: H <- exp(cs_end) H + exp(cs_end - ref) B (w o x).
+    f32x4 T[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        T[j] = mfma16(bop[kb][j], xh[kb], T[j]);
+        T[j] = mfma16(bop[kb][j], xl[kb], T[j]);
+      }
+    }
+    const float alpha = exp2_hw(cs_end * kLog2e);
+    const float beta = sep ? exp2_hw((cs_end - ref) * kLog2e) : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) H[j][q] = __builtin_fmaf(H[j][q], alpha, T[j][q] * beta);
+    write_slice(Next());
+  };
+
+  LL la, lb;
+  write_slice(std::integral_constant<int, 0>());
+  issue(std::integral_constant<int, 0>(), 0, la);
+  for (int c = 0; c < p.nblocks; c += 2) {
+    block(std::integral_constant<int, 0>(), c, la, lb);
+    if (c + 1 < p.nblocks) block(std::integral_constant<int, 1>(), c + 1, lb, la);
+  }
+
+  if (fs && wave_on) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *reinterpret_cast<f32x4*>(fs + 32 * nq + 16 * j + 4 * g) = H[j];
+  }
+}
+
 template <int N, bool kVec>
 int launch_n(const SsdArgs& a, const SsdParams& p, hipStream_t s) {
-  constexpr int kNS = StateSplit<N>::kNS;
-  const dim3 pgrid = dim3(unsigned(p.nblocks * a.batch));
-  hipLaunchKernelGGL((ssd_prep_kernel<N, kVec>), pgrid, dim3(256), 0, s, p);
+  const int64_t records = a.batch * a.nheads * p.nblocks;
+  const int n_prep = int(p.nblocks * a.batch);
+  const dim3 pgrid = dim3(unsigned(n_prep + (records + 3) / 4));
+  hipLaunchKernelGGL((ssd_prep_kernel<N, kVec>), pgrid, dim3(256), 0, s, p, n_prep, records);
   const dim3 grid = dim3(unsigned((a.headdim + 31) / 32 * a.nheads * a.batch));
-  hipLaunchKernelGGL((ssd_fwd_kernel<N, kVec, kNS>), grid, dim3(128 * kNS), 0, s, p);
+  if constexpr (N <= 128) {
+    constexpr int kNS = ChunkLayout<N>::kNS;
+    hipLaunchKernelGGL((ssd_chunk_kernel<N, kVec>), grid, dim3(128 * kNS), 0, s, p);
+  } else {
+    constexpr int kNS = StateSplit<N>::kNS;
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, kVec, kNS>), grid, dim3(128 * kNS), 0, s, p);
+  }
   return int(hipGetLastError());
 }
 
@@ -671,6 +1077,7 @@ int launch_ssd_fwd(const SsdArgs& a, void* stream) {
   p.initial_state = a.initial_state ? 1 : 0;
   p.G = static_cast<uint16_t*>(a.workspace);
   p.CTp = p.G + size_t(a.batch) * p.nblocks * kQ * kQ;
+  p.steps = reinterpret_cast<float*>(p.CTp + size_t(a.batch) * p.nblocks * kQ * a.dstate);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (a.dstate) {
     case 64:

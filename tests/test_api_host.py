@@ -142,11 +142,14 @@ def ssd_call(**kw):
 
 
 def test_ssd_workspace_size():
-    # per (batch row, 64-step block): 64x64 bf16 of G and 64 x dstate bf16 of C^T
-    assert ssm.ssm_ssd_workspace_bytes(2, 128, 2048) == 2 * 32 * (64 * 64 * 2 + 64 * 128 * 2)
-    assert ssm.ssm_ssd_workspace_bytes(1, 64, 65) == 2 * (64 * 64 * 2 + 64 * 64 * 2)
-    assert ssm.ssm_ssd_workspace_bytes(3, 64, 0) == 0
-    assert ssm.ssm_ssd_workspace_bytes(-1, 64, 1) == -1
+    # per (batch row, block) G and C^T in bf16; per (batch row, head, block) 4 x 64 fp32
+    assert ssm.ssm_ssd_workspace_bytes(2, 32, 128, 2048) == \
+        2 * 32 * (64 * 64 * 2 + 64 * 128 * 2) + 2 * 32 * 32 * 1024
+    assert ssm.ssm_ssd_workspace_bytes(1, 3, 64, 65) == 2 * (64 * 64 * 2 + 64 * 64 * 2) + 3 * 2 * 1024
+    assert ssm.ssm_ssd_workspace_bytes(3, 2, 64, 0) == 0
+    assert ssm.ssm_ssd_workspace_bytes(-1, 2, 64, 1) == -1
+    assert ssm.ssm_ssd_workspace_bytes(1, -1, 64, 1) == -1
+    assert ssm.ssm_ssd_workspace_bytes(1 << 40, 1 << 20, 256, 1 << 20) == -1
 
 
 @pytest.mark.parametrize("kw", [

@@ -149,8 +149,8 @@ def test_graph_chunked_forward_new_inputs():
 
 
 def test_graph_ssd_forward():
-    """The two SSD kernels (block products, then the per-head pass) captured with a
-    workspace held by the caller."""
+    """The SSD kernels (step factors, block products, then the per-head pass) captured
+    with a workspace held by the caller."""
     t = torch()
     w = SSD_WORKLOADS["ssd_tiny"].with_(batch=2, nheads=4, headdim=64, dstate=128,
                                         seqlen=700, initial_state=True, seed=503)
@@ -158,8 +158,8 @@ def test_graph_ssd_forward():
     inp = make_ssd_inputs(w)
     g = {k: dev(inp[k], "bf16") for k in ("x", "dt", "B", "C", "z")}
     f = {k: dev(inp[k], "f32") for k in ("A", "D", "dt_bias", "h0")}
-    ws = t.empty(ssm.ssm_ssd_workspace_bytes(w.batch, w.dstate, w.seqlen), dtype=t.uint8,
-                 device="cuda")
+    ws = t.empty(ssm.ssm_ssd_workspace_bytes(w.batch, w.nheads, w.dstate, w.seqlen),
+                 dtype=t.uint8, device="cuda")
     out = t.empty_like(g["x"])
     fin = t.empty_like(f["h0"])
 

@@ -109,7 +109,7 @@ def test_ssd_deterministic_and_workspace_reuse():
                                         seed=1300)
     announce(w.describe() + " determinism")
     inp = make_ssd_inputs(w)
-    ws = t.empty(ssm.ssm_ssd_workspace_bytes(2, 128, 1500), dtype=t.uint8, device="cuda")
+    ws = t.empty(ssm.ssm_ssd_workspace_bytes(2, 4, 128, 1500), dtype=t.uint8, device="cuda")
     a = run_gpu(inp, workspace=ws)
     b = run_gpu(inp, workspace=ws)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
@@ -141,3 +141,22 @@ def test_ssd_workload_full():
     announce(w.describe())
     inp = make_ssd_inputs(w)
     check(run_gpu(inp), run_oracle(inp), w.describe())
+
+
+@pytest.mark.parametrize("dstate", [64, 128])
+def test_ssd_large_decay_blocks(dstate):
+    """Blocks whose decay exceeds the separable form's span (120 in natural-log units; the
+    kernel then forms the decayed block matrix) beside blocks within it. A is set per head
+    so that a head's median 64-step block decays by 0.3, 1, 3 and 10 times that span: the
+    second head has blocks on both sides of it."""
+    w = SSD_WORKLOADS["ssd_tiny"].with_(batch=2, nheads=4, headdim=32, dstate=dstate,
+                                        seqlen=700, initial_state=True, seed=1500 + dstate)
+    announce(f"{w.describe()} large decay")
+    inp = make_ssd_inputs(w)
+    raw = widen(inp["dt"], "bf16") + inp["dt_bias"][None, :, None]
+    step = np.where(raw <= 20, np.logaddexp(0.0, raw), raw)[..., :640]
+    block_sum = np.median(step.reshape(2, 4, 10, 64).sum(-1), axis=(0, 2))   # per head
+    inp["A"] = (-120.0 * np.array([0.3, 1.0, 3.0, 10.0]) / block_sum).astype(np.float32)
+    span = -(step * inp["A"][None, :, None]).reshape(2, 4, 10, 64).sum(-1)
+    assert (span[:, 1] > 120).any() and (span[:, 1] <= 120).any()
+    check(run_gpu(inp), run_oracle(inp), f"{w.describe()} large decay")
