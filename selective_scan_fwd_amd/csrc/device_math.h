@@ -35,11 +35,13 @@ __device__ __forceinline__ float gate_f(float y, float z) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round to bf16, nearest-even (v_cvt_pk_bf16_f32 on gfx950), two values per dword.
+// Round to bf16, nearest-even, two values per dword. Converted as one two-element vector,
+// this is a single v_cvt_pk_bf16_f32 on gfx950; two scalar conversions would cost two of
+// them plus a shift and an or to merge the halves.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 l = (__bf16)lo, h = (__bf16)hi;
-  return uint32_t(__builtin_bit_cast(uint16_t, l)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, h)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 }  // namespace ssm
