@@ -116,6 +116,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (readlane(v, 15) + readlane(v, 31)) + (readlane(v, 47) + readlane(v, 63));
 }
 
+// Sum over the 64 lanes, complete in lane 63: DPP row_shr partial sums inside each row, then
+// row_bcast:15 and row_bcast:31 carry the row totals up (no readlanes).
+__device__ __forceinline__ float wave_sum_to_last(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
 // kMask: read a padding mask (its own instantiation: the unmasked kernel's register count
@@ -226,18 +238,17 @@ __global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
       // every h_t anyway. dout, z and the biased step size are read again after the loop
       // (from L2) rather than kept live across it.
       float y[T];
+#pragma unroll
+      for (int j = 0; j < T; ++j) y[j] = Dd * uv[j];
       if (p.z) {
 #pragma unroll
-        for (int j = 0; j < T; ++j) {
-          dyv[j] = dov[j] * zv[j] * sigmoid_f(zv[j]);
-          y[j] = Dd * uv[j];
-        }
+        for (int j = 0; j < T; ++j) dyv[j] = dov[j] * zv[j] * sigmoid_f(zv[j]);
       }
 #pragma unroll
       for (int j = 0; j < T; ++j) {
         dD_acc = __builtin_fmaf(dyv[j], uv[j], dD_acc);
-        gdu[j] = Dd * dyv[j];
-        gds[j] = 0.0f;
+        gdu[j] = 0.0f;  // sum over states of g B (du and the step size share it)
+        gds[j] = 0.0f;  // sum over states of g A a h_{t-1}
       }
 
       for (int n = 0; n < N; ++n) {
@@ -265,7 +276,8 @@ __global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
             for (int j = 0; j < T; ++j) {
               hh = __builtin_fmaf(dA[j], hh, (sv[j] * uv[j]) * Bv[j]);
               h[j] = hh;
-              if (p.z) y[j] = __builtin_fmaf(Cv[j], hh, y[j]);
+              y[j] = __builtin_fmaf(Cv[j], hh, y[j]);  // read only with a gate; a select
+                                                       // per step would cost more
             }
           }
           // adjoint: fold the lane's steps from the right, scan from lane 63 down
@@ -287,35 +299,39 @@ __global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
             const float t1 = dA[j] * hp;
             acc[par][0][wave][j * kPitch + lane] = g * (sv[j] * uv[j]);  // dB
             acc[par][1][wave][j * kPitch + lane] = dyv[j] * h[j];        // dC
-            gdu[j] = __builtin_fmaf(g, sv[j] * Bv[j], gdu[j]);
-            gds[j] = __builtin_fmaf(g, __builtin_fmaf(An, t1, Bv[j] * uv[j]), gds[j]);
-            dAn = __builtin_fmaf(g * t1, sv[j], dAn);
+            const float q = g * t1;
+            gdu[j] = __builtin_fmaf(g, Bv[j], gdu[j]);
+            gds[j] = __builtin_fmaf(q, An, gds[j]);
+            dAn = __builtin_fmaf(q, sv[j], dAn);
             v = dA[j] * g;  // e_t = a_t g_t
           }
-          dAn = wave_sum(dAn);
+          dAn = readlane(wave_sum_to_last(dAn), 63);
           dA_l = (lane == n) ? dA_l + dAn : dA_l;
         }
         __syncthreads();  // every channel's share of state n is in acc[par]
-        // Add the workgroup's sums for state n into dB and dC, one step per thread. The
-        // buffer is written again two states later, after the next barrier, which no
-        // thread passes before finishing this loop. Every active wave overwrites its rows
-        // for every state; inactive waves' rows stay zero.
-        for (int i = tid; i < kChunk; i += 64 * K) {
-          const int ln = i / T, j = i - ln * T;
-          const int t = c * kChunk + i;
-          float vb = 0.0f, vc = 0.0f;
-#pragma unroll
-          for (int k = 0; k < K; ++k) {
-            vb += acc[par][0][k][j * kPitch + ln];
-            vc += acc[par][1][k][j * kPitch + ln];
-          }
-          if (t < L) {
-            const int64_t o = (int64_t(b) * N + n) * L + t;
-            unsafeAtomicAdd(&p.dB[o], vb);
-            unsafeAtomicAdd(&p.dC[o], vc);
-          }
+        // Add the workgroup's sums for state n into dB and dC: one (gradient, step) item per
+        // thread and pass, dB items first (whole waves take the same gradient). The buffer is
+        // written again two states later, after the next barrier, which no thread passes
+        // before finishing this loop. Every active wave overwrites its rows for every state;
+        // inactive waves' rows stay zero.
+        for (int i = tid; i < 2 * kChunk; i += 64 * K) {
+          const int wc = i >= kChunk ? 1 : 0;  // 0: dB, 1: dC
+          const int st = i - wc * kChunk;
+          const int ln = st / T, j = st - ln * T;
+          const int t = c * kChunk + st;
+          float v = 0.0f;
+#pragma unroll 4  // fully unrolled, the K loads in flight would push past 128 registers
+          for (int k = 0; k < K; ++k) v += acc[par][wc][k][j * kPitch + ln];
+          if (t < L) unsafeAtomicAdd(&(wc ? p.dC : p.dB)[(int64_t(b) * N + n) * L + t], v);
         }
         ++it;
+      }
+      // du_t = s_t sum_n g B + D dy_t and ds_t = sum_n g (A a h_{t-1} + B u_t), from the two
+      // sums over the states.
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        gds[j] = __builtin_fmaf(uv[j], gdu[j], gds[j]);
+        gdu[j] = __builtin_fmaf(sv[j], gdu[j], Dd * dyv[j]);
       }
       if (p.z) {
         float dz2[T], zz[T];
@@ -423,7 +439,10 @@ int launch_scan_bwd(const BwdArgs& a, void* stream) {
   if (st == 0 && a.dD) st = launch_fill_zero(a.dD, a.dim, stream);
   if (st == 0 && a.dbias) st = launch_fill_zero(a.dbias, a.dim, stream);
   if (st != 0) return st;
-  if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, 8>(a, s);
+  // bf16: 16 channels per workgroup, half the dB/dC atomics of 8 at the same 4 waves per SIMD
+  // (one 16-wave workgroup per CU; its per-wave rows take 144 KB of LDS). fp32 keeps 8: at
+  // 16 its masked kernel spills past 128 registers.
+  if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, 16>(a, s);
   return launch_bwd_typed<float, 8, 8>(a, s);
 }
 
