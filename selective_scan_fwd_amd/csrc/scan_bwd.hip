@@ -382,6 +382,19 @@ __global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
   }
 }
 
+// Up to five float arrays to zero (count 0: skipped); grid.y picks the array.
+struct ZeroList {
+  float* p[5];
+  int64_t n[5];
+};
+
+__global__ __launch_bounds__(256) void fill_zero_many_kernel(ZeroList z) {
+  float* p = z.p[blockIdx.y];
+  const int64_t n = z.n[blockIdx.y];
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+}
+
 template <typename Elem, int T, int K>
 int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   BParams p;
@@ -432,13 +445,28 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
 
 int launch_scan_bwd(const BwdArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The channel- and batch-summed gradients are accumulated with atomics.
-  int st = launch_fill_zero(a.dA, a.dim * a.dstate, stream);
-  if (st == 0) st = launch_fill_zero(a.dB, a.batch * a.dstate * a.seqlen, stream);
-  if (st == 0) st = launch_fill_zero(a.dC, a.batch * a.dstate * a.seqlen, stream);
-  if (st == 0 && a.dD) st = launch_fill_zero(a.dD, a.dim, stream);
-  if (st == 0 && a.dbias) st = launch_fill_zero(a.dbias, a.dim, stream);
-  if (st != 0) return st;
+  // The channel- and batch-summed gradients are accumulated with atomics: zero all five in
+  // one launch (five small launches cost more than their bytes).
+  ZeroList z;
+  z.p[0] = a.dA;
+  z.n[0] = a.dim * a.dstate;
+  z.p[1] = a.dB;
+  z.n[1] = a.batch * a.dstate * a.seqlen;
+  z.p[2] = a.dC;
+  z.n[2] = z.n[1];
+  z.p[3] = a.dD;
+  z.n[3] = a.dD ? a.dim : 0;
+  z.p[4] = a.dbias;
+  z.n[4] = a.dbias ? a.dim : 0;
+  int64_t most = 0;
+  for (int k = 0; k < 5; ++k) most = z.n[k] > most ? z.n[k] : most;
+  if (most > 0) {
+    int64_t gx = (most + 1023) / 1024;  // about four stores per thread
+    gx = gx < 1 ? 1 : (gx > 4096 ? 4096 : gx);
+    hipLaunchKernelGGL(fill_zero_many_kernel, dim3(unsigned(gx), 5), dim3(256), 0, s, z);
+    const int st = int(hipGetLastError());
+    if (st != 0) return st;
+  }
   // bf16: 16 channels per workgroup, half the dB/dC atomics of 8 at the same 4 waves per SIMD
   // (one 16-wave workgroup per CU; its per-wave rows take 144 KB of LDS). fp32 keeps 8: at
   // 16 its masked kernel spills past 128 registers.
