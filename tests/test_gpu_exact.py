@@ -1,6 +1,7 @@
 """GPU checks with exact answers, and properties that hold at any size.
 
-  * the pages' prefix-sum example and a 65536-step exact carry: bitwise;
+  * the pages' prefix-sum example and a 65536-step exact carry: bitwise; the same carry at
+    the largest B/C rows the API accepts (2^31 - 128 bytes per batch row);
   * the wave-level combine routine on integer pairs: bitwise, every lane;
   * run-to-run determinism: bitwise;
   * chaining two calls through final_state, delta = 0, zero input, B = 0, empty sizes.
@@ -50,6 +51,31 @@ def test_long_exact_carry_bitwise(io):
     for d in range(3):
         assert np.array_equal(out[0, d], expect)
     assert np.all(fin[0, :, 0] == L)
+
+
+@pytest.mark.slow
+def test_exact_carry_at_the_offset_limit():
+    """The largest B/C rows the API accepts: 64 states x (2^24 - 1) steps of bf16 per batch
+    row is 2^31 - 128 bytes, the top of the 32-bit offsets inside a row. u = 1, A = 0,
+    delta = 1 and B = C = e_0 make every output the exact step count t + 1 (below 2^24,
+    so exact in float32; bf16 out is its round-to-nearest-even), in both batch rows."""
+    t = torch()
+    L, N, batch, dim = (1 << 24) - 1, 64, 2, 2
+    announce(f"exact carry at the offset limit: b{batch} d{dim} N{N} L{L} bf16")
+    u = t.ones((batch, dim, L), dtype=t.bfloat16, device="cuda")
+    delta = t.ones_like(u)
+    Bm = t.zeros((batch, N, L), dtype=t.bfloat16, device="cuda")
+    Bm[:, 0] = 1.0
+    Cm = Bm.clone()
+    A = t.zeros((dim, N), dtype=t.float32, device="cuda")
+    out, fin = ssm.scan(u, delta, A, Bm, Cm)
+    t.cuda.synchronize()
+    idx = t.arange(1, L + 1, device="cuda", dtype=t.float32)
+    expect = idx.to(t.bfloat16)          # round-to-nearest-even of the exact t + 1
+    for b in range(batch):
+        for d in range(dim):
+            assert t.equal(out[b, d].view(t.int16), expect.view(t.int16)), (b, d)
+    assert t.all(fin[:, :, 0] == L) and not t.any(fin[:, :, 1:])
 
 
 def test_wave_combine_lane_wiring_bitwise():
