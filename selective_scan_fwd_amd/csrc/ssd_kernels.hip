@@ -750,6 +750,12 @@ __global__ __launch_bounds__(128 * ChunkLayout<N>::kNS) void ssd_chunk_kernel(Ss
   __shared__ __attribute__((aligned(16))) uint4 sG0[kQ * 8], sG1[kQ * 8];
   __shared__ __attribute__((aligned(16))) uint4 sXZ0[2 * kXW], sXZ1[2 * kXW];
   __shared__ __attribute__((aligned(16))) uint4 sH0[2][kNS][2][64], sH1[2][kNS][2][64];
+  // At 128 states each wave copies its block's 1 KB step record by DMA into a slot of its own
+  // (dynamic LDS, kWaves KB) instead of six per-lane loads: the per-lane loads repeat each
+  // address across lanes and crowd the vector memory path right after the barrier. At 64
+  // states the stages alone are 80 KB, the most that lets two workgroups share a CU.
+  constexpr bool kStepDma = N == 128;
+  extern __shared__ __attribute__((aligned(16))) uint4 sStepDyn[];  // [kWaves][64]
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
@@ -843,15 +849,21 @@ __global__ __launch_bounds__(128 * ChunkLayout<N>::kNS) void ssd_chunk_kernel(Ss
       row_copy(xbuf, xrow0, w, c, sXZs, ld.xst[0], xvalid);
       row_copy(zbuf, xrow0, w, c, sXZs + kXW, ld.xst[kXZInstr - 1], zvalid);
     }
-    const uint32_t rb = c < p.nblocks ? uint32_t(c) * (4 * kQ * 4) : kOob;
-    const bool ok = c < p.nblocks;
+    if constexpr (kStepDma) {
+      const uint32_t off = c < p.nblocks ? uint32_t(c) * (4 * kQ * 4) + uint32_t(l) * 16u : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sbuf.r, (lds_void_t*)&sStepDyn[w * 64], 16, off, 0,
+                                               0, 0);
+    } else {
+      const uint32_t rb = c < p.nblocks ? uint32_t(c) * (4 * kQ * 4) : kOob;
+      const bool ok = c < p.nblocks;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      ld.w[q] = ld_f4(sbuf, ok ? rb + 4u * uint32_t(32 * (q >> 1) + 8 * g + 4 * (q & 1)) : kOob);
+      for (int q = 0; q < 4; ++q)
+        ld.w[q] = ld_f4(sbuf, ok ? rb + 4u * uint32_t(32 * (q >> 1) + 8 * g + 4 * (q & 1)) : kOob);
 #pragma unroll
-    for (int k = 0; k < kOwn; ++k)
-      ld.e[k] = ld_f4(sbuf, ok ? rb + 4u * uint32_t(kQ + 16 * (nq + kNS * k) + 4 * g) : kOob);
-    ld.cse = ld_f1(sbuf, ok ? rb + 4u * uint32_t(2 * kQ + kQ - 1) : kOob);
+      for (int k = 0; k < kOwn; ++k)
+        ld.e[k] = ld_f4(sbuf, ok ? rb + 4u * uint32_t(kQ + 16 * (nq + kNS * k) + 4 * g) : kOob);
+      ld.cse = ld_f1(sbuf, ok ? rb + 4u * uint32_t(2 * kQ + kQ - 1) : kOob);
+    }
   };
 
   auto block = [&](auto tag, int c, LL& cur, LL& nxt) {
@@ -867,7 +879,21 @@ __global__ __launch_bounds__(128 * ChunkLayout<N>::kNS) void ssd_chunk_kernel(Ss
     // This block's copies have landed (the previous block's output stores may still be in
     // flight: vector memory operations complete in issue order), then one barrier
     // publishes them and the H slices written at the previous block's end.
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStores) : "memory");
+    // The builtin, unlike an asm wait, is seen by the compiler's own wait insertion, which
+    // then knows these copies have landed. Operand: vmcnt = kStores in bits 3:0 (its high
+    // bits 15:14 zero); expcnt (6:4) and lgkmcnt (11:8) at their maxima, i.e. not waited on.
+    static_assert(kStores < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0xF70 | kStores);
+    asm volatile("" ::: "memory");
+    if constexpr (kStepDma) {
+      // This wave's step record, landed with the copies above.
+      static_assert(kOwn == 1, "one output tile per wave at 128 states");
+      const float4* rec = reinterpret_cast<const float4*>(&sStepDyn[w * 64]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cur.w[q] = rec[8 * (q >> 1) + 2 * g + (q & 1)];
+      cur.e[0] = rec[(kQ + 16 * nq + 4 * g) / 4];
+      cur.cse = reinterpret_cast<const float*>(rec)[2 * kQ + kQ - 1];
+    }
     if constexpr (!kVec) {
       uint4* sBw = bb == 0 ? sB0 : sB1;
       uint4* sXZw = bb == 0 ? sXZ0 : sXZ1;
@@ -1020,6 +1046,11 @@ __global__ __launch_bounds__(128 * ChunkLayout<N>::kNS) void ssd_chunk_kernel(Ss
   LL la, lb;
   write_slice(std::integral_constant<int, 0>());
   issue(std::integral_constant<int, 0>(), 0, la);
+  // The block-top wait leaves the last kStores operations in flight, which from the second
+  // block on are the previous block's output stores. The first block has none behind its
+  // copies: waiting for them in full here lets the compiler see, on entry to the loop, that
+  // nothing but stores can be pending, so it adds no full wait of its own inside the loop.
+  if constexpr (kStepDma) __builtin_amdgcn_s_waitcnt(0xF70);
   for (int c = 0; c < p.nblocks; c += 2) {
     block(std::integral_constant<int, 0>(), c, la, lb);
     if (c + 1 < p.nblocks) block(std::integral_constant<int, 1>(), c + 1, lb, la);
@@ -1041,7 +1072,8 @@ int launch_n(const SsdArgs& a, const SsdParams& p, hipStream_t s) {
   const dim3 grid = dim3(unsigned((a.headdim + 31) / 32 * a.nheads * a.batch));
   if constexpr (N <= 128) {
     constexpr int kNS = ChunkLayout<N>::kNS;
-    hipLaunchKernelGGL((ssd_chunk_kernel<N, kVec>), grid, dim3(128 * kNS), 0, s, p);
+    const size_t step_lds = N == 128 ? size_t(2 * kNS) * 1024 : 0;  // one 1 KB slot per wave
+    hipLaunchKernelGGL((ssd_chunk_kernel<N, kVec>), grid, dim3(128 * kNS), step_lds, s, p);
   } else {
     constexpr int kNS = StateSplit<N>::kNS;
     hipLaunchKernelGGL((ssd_fwd_kernel<N, kVec, kNS>), grid, dim3(128 * kNS), 0, s, p);
