@@ -310,14 +310,23 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
 #pragma unroll
         for (int e = 0; e < kVec; ++e) {
           const int j = q * kVec + e;
-          const float x = dr[e] + bias_d;
-          float s = p.softplus ? softplus_f(x) : x;
-          if (tail) s = (tb + j < L) ? s : 0.0f;  // steps past L: identity (dA = 1, dBu = 0)
-          dt[j] = s;
-          du[j] = s * uv[e];
+          dt[j] = dr[e] + bias_d;
+          du[j] = uv[e];  // u for now; times the step size below
           y[j] = Dd * uv[e];
         }
       }
+      // Each flag is tested once per chunk, around whole loops: a test per step would be
+      // turned into a select per step, paid on every chunk.
+      if (p.softplus) {
+#pragma unroll
+        for (int j = 0; j < T; ++j) dt[j] = softplus_f(dt[j]);
+      }
+      if (tail) {  // steps past L: identity (dA = 1, dBu = 0)
+#pragma unroll
+        for (int j = 0; j < T; ++j) dt[j] = (tb + j < L) ? dt[j] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < T; ++j) du[j] *= dt[j];
       if constexpr (kMask) {
         // A padding step keeps the state: a zero step size makes it the identity (dA = 1,
         // dBu = 0) while y still reads the state.
