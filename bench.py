@@ -264,11 +264,15 @@ def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     ptr = lambda t: None if t is None else t.data_ptr()
+    # The calls run one after another on one stream, so they can share one workspace.
+    ws_bytes = 0 if args.bwd_atomics else ssm.ssm_scan_bwd_workspace_bytes(
+        w.batch, w.dim, w.dstate, w.seqlen, flags)
+    ws = torch.empty((max(ws_bytes, 1),), device=dev, dtype=torch.uint8) if ws_bytes else None
     calls = [(ptr(s["u"]), ptr(s["delta"]), ptr(s["A"]), ptr(s["B"]), ptr(s["C"]), ptr(s["D"]),
               ptr(s["z"]), ptr(s["delta_bias"]), None, flags, ptr(s["ckpt"]), ptr(s["dout"]),
               ptr(s["dfinal"]), ptr(s["du"]), ptr(s["ddelta"]), ptr(s["dA"]), ptr(s["dB"]),
               ptr(s["dC"]), ptr(s["dD"]), ptr(s["dz"]), ptr(s["dbias"]), ptr(s["dh0"]),
-              w.batch, w.dim, w.dstate, w.seqlen, sp) for s in sets]
+              ptr(ws), ws_bytes, w.batch, w.dim, w.dstate, w.seqlen, sp) for s in sets]
     fn = ssm.lib().ssm_scan_bwd
 
     def launch(i):
@@ -292,7 +296,9 @@ def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
            "work": f"{set_bytes} algorithmic bytes per launch"}
     main_, other = (("alu", alu), ("hbm", hbm)) if t_alu >= t_hbm else (("hbm", hbm), ("alu", alu))
     roofline = {"bound": main_[0], **main_[1],
-                "traffic": load_traffic(args.workload, "bwd"), "kernel": "scan_bwd_kernel",
+                "traffic": None if args.bwd_atomics else load_traffic(args.workload, "bwd"),
+                "kernel": ("scan_bwd_kernel (float atomics)" if args.bwd_atomics else
+                           "scan_bwd_kernel + bwd_reduce_kernel (one call)"),
                 "kernel_hash": kernel_hash("bwd"),
                 "floor_us": {"alu": round(t_alu * 1e6, 3), "hbm": round(t_hbm * 1e6, 3)},
                 other[0]: other[1]}
@@ -305,7 +311,9 @@ def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
         "data": "synthetic (seeded numpy PCG64 inputs; dout, dfinal from a seeded torch generator)",
         "config": {"workload": w.describe(), "direction": "bwd", "batch": w.batch,
                    "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen, "io_dtype": w.io,
-                   "gate": w.gate, "buffer_sets": nsets, "algorithmic_bytes": set_bytes},
+                   "gate": w.gate, "buffer_sets": nsets, "algorithmic_bytes": set_bytes,
+                   "summed_gradients": ("float atomics" if args.bwd_atomics else
+                                        f"workspace of {ws_bytes} bytes, fixed-order sums")},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tuples_per_s": round(w.tuples * K / wall, 1),
         "kernel_us": {"mean": round(avg_ms * 1e3, 3),
@@ -563,6 +571,9 @@ def main() -> int:
     ap.add_argument("--direction", choices=("fwd", "bwd"), default="fwd",
                     help="fwd: the forward scan (the default, headline); bwd: the backward "
                          "pass from the forward's saved states")
+    ap.add_argument("--bwd-atomics", action="store_true",
+                    help="with --direction bwd: sum dA, dB, dC, dD and dbias with float atomics "
+                         "(no workspace) instead of the reproducible workspace sums")
     ap.add_argument("--decode-loop", type=int, default=0, metavar="T",
                     help="with --workload decode: time a loop of T one-token calls that carry "
                          "the state in place, launched eagerly and as one captured HIP graph")

@@ -167,9 +167,18 @@ SSM_API int ssm_scan_fwd_masked(const void* u, const void* delta, const float* A
  *                wanted (ignored when D or delta_bias is NULL)
  *   dh0          [batch, dim, dstate]  fp32, gradient of the initial state; NULL = not
  *                wanted
- * The summed gradients are accumulated with floating-point atomics, so they are not
- * bitwise reproducible from run to run (within fp32 rounding of one another); du, ddelta,
- * dz and dh0 are. Scratch: none beyond LDS. Errors as for ssm_scan_fwd.
+ * workspace: NULL, or ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, flags) bytes
+ * (workspace_bytes, at least that), 256-byte aligned, device scratch owned by the caller,
+ * overlapping no other argument; its contents are overwritten and need not be kept between
+ * calls, and calls that share it must not overlap in time.
+ * The summed gradients (dA, dB, dC, dD, dbias) add up contributions of many channels or
+ * batch rows. With a workspace, each workgroup stores its partial sums there and a second
+ * launch adds them in a fixed order: every output is bitwise reproducible. Without one they
+ * are accumulated with floating-point atomics (after a zero fill), which needs no scratch but
+ * is slower and not reproducible from run to run (within fp32 rounding of one another); du,
+ * ddelta, dz and dh0 are reproducible either way. Errors as for ssm_scan_fwd, plus
+ * SSM_ERR_INVALID_ARG for a workspace that is too small or overlaps an argument and
+ * SSM_ERR_MISALIGNED for one not 256-byte aligned.
  */
 SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z,
@@ -177,13 +186,23 @@ SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const
                          const float* chunk_states,
                          const void* dout, const float* dfinal, void* du, void* ddelta,
                          float* dA, float* dB, float* dC, float* dD, void* dz, float* dbias,
-                         float* dh0, int64_t batch, int64_t dim, int64_t dstate,
-                         int64_t seqlen, void* stream);
+                         float* dh0, void* workspace, int64_t workspace_bytes, int64_t batch,
+                         int64_t dim, int64_t dstate, int64_t seqlen, void* stream);
+
+/*
+ * Bytes of workspace ssm_scan_bwd needs for reproducible sums: each workgroup's sums of dB
+ * and dC over its channels (16 channels per workgroup for bf16 storage, 8 for fp32, set by
+ * the storage type in flags bits 0-1), 2 x dstate x seqlen fp32 per workgroup, and dA, dD
+ * and dbias per batch row. 0 for empty problems; -1 for negative sizes, an unknown storage
+ * type or a size past int64.
+ */
+SSM_API int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate,
+                                             int64_t seqlen, uint32_t flags);
 
 /* Static, human-readable text for a status code (never NULL). */
 SSM_API const char* ssm_scan_strerror(int status);
 
-/* Version of this ABI (bumped on any incompatible change): 2. */
+/* Version of this ABI (bumped on any incompatible change): 3. */
 SSM_API int ssm_scan_abi_version(void);
 
 /*

@@ -37,7 +37,8 @@ SSM_CKPT_INTERVAL = 512
 
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_strerror", "ssm_scan_abi_version",
             "ssm_scan_debug_wave_combine", "ssm_scan_ckpt_count", "ssm_scan_fwd_ckpt",
-            "ssm_scan_fwd_masked", "ssm_scan_bwd", "ssm_ssd_workspace_bytes", "ssm_ssd_fwd")
+            "ssm_scan_fwd_masked", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
+            "ssm_ssd_workspace_bytes", "ssm_ssd_fwd")
 
 _lib = None
 
@@ -76,8 +77,11 @@ def lib() -> ctypes.CDLL:
                                       vp, vp, i64, i64, i64, i64, vp]
     L.ssm_scan_fwd_masked.restype = ctypes.c_int
     L.ssm_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
-                               vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]
+                               vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                               vp]
     L.ssm_scan_bwd.restype = ctypes.c_int
+    L.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_uint32]
+    L.ssm_scan_bwd_workspace_bytes.restype = i64
     L.ssm_ssd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     L.ssm_ssd_workspace_bytes.restype = i64
     L.ssm_ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
@@ -112,11 +116,15 @@ def ssm_scan_fwd_masked(u, delta, A, B, C, D, z, delta_bias, mask, flags, out, f
 
 
 def ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, mask, flags, chunk_states, dout, dfinal,
-                 du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch, dim, dstate, seqlen,
-                 stream) -> int:
+                 du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, workspace, workspace_bytes, batch,
+                 dim, dstate, seqlen, stream) -> int:
     return lib().ssm_scan_bwd(u, delta, A, B, C, D, z, delta_bias, mask, flags, chunk_states,
-                              dout, dfinal, du, ddelta, dA, dB, dC, dD, dz, dbias, dh0, batch,
-                              dim, dstate, seqlen, stream)
+                              dout, dfinal, du, ddelta, dA, dB, dC, dD, dz, dbias, dh0,
+                              workspace, workspace_bytes, batch, dim, dstate, seqlen, stream)
+
+
+def ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, flags) -> int:
+    return lib().ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, flags)
 
 
 def ssm_scan_strerror(status: int) -> str:
@@ -270,11 +278,17 @@ def scan_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplu
 
 
 def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_bias=None,
-                  delta_softplus: bool = False, dfinal=None, want_dh0: bool = True, mask=None
+                  delta_softplus: bool = False, dfinal=None, want_dh0: bool = True, mask=None,
+                  deterministic: bool = True, workspace=None
                   ) -> Dict[str, Optional["torch.Tensor"]]:
     """Gradients of sum(dout * out) + sum(dfinal * final_state) for the forward on the same
     inputs. Returns du, ddelta, dz (u's dtype), dA, dB, dC, dD, dbias, dh0 (float32; None
-    where the input is absent or, for dh0, not wanted)."""
+    where the input is absent or, for dh0, not wanted).
+
+    deterministic: sum dA, dB, dC, dD and dbias through a workspace in a fixed order
+    (bitwise reproducible; ssm_scan_bwd_workspace_bytes of device memory, allocated here
+    unless ``workspace``, a uint8 device tensor at least that large, is given); False: float
+    atomics, no workspace."""
     import torch
 
     flags, batch, dim, dstate, seqlen = _check(u, delta, A, B, C, D, z, delta_bias, None)
@@ -302,12 +316,26 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
          "dD": None if D is None else torch.empty((dim,), **f32),
          "dbias": None if delta_bias is None else torch.empty((dim,), **f32),
          "dh0": torch.empty((batch, dim, dstate), **f32) if want_dh0 else None}
+    ws_bytes = 0
+    if deterministic:
+        need = ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, flags)
+        if need < 0:
+            raise SsmScanError(SSM_ERR_UNSUPPORTED)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), device=dev, dtype=torch.uint8)
+        elif (workspace.dtype != torch.uint8 or workspace.device != dev
+              or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous uint8 tensor on u's device")
+        ws_bytes = workspace.numel()
+    else:
+        workspace = None
     status = ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                           _ptr(delta_bias), _ptr(mask), flags, _ptr(chunk_states), _ptr(dout),
                           _ptr(dfinal),
                           _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                           _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dbias"]),
-                          _ptr(g["dh0"]), batch, dim, dstate, seqlen, _stream_of(dev))
+                          _ptr(g["dh0"]), _ptr(workspace), ws_bytes, batch, dim, dstate, seqlen,
+                          _stream_of(dev))
     if status != SSM_OK:
         raise SsmScanError(status)
     return g

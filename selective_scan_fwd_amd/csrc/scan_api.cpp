@@ -22,7 +22,7 @@ using ssm_api::span;
 
 extern "C" {
 
-int ssm_scan_abi_version(void) { return 2; }
+int ssm_scan_abi_version(void) { return 3; }
 
 const char* ssm_scan_strerror(int status) {
   switch (status) {
@@ -177,12 +177,25 @@ int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const vo
 
 int64_t ssm_scan_ckpt_count(int64_t seqlen) { return ckpt_count(seqlen); }
 
+int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                                     uint32_t flags) {
+  if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return -1;
+  const uint32_t io = flags & SSM_IO_MASK;
+  if (io != SSM_IO_F32 && io != SSM_IO_BF16) return -1;
+  ssm::BwdWorkspace w;
+  if (!ssm::bwd_workspace(batch, dim, dstate, seqlen,
+                          io == SSM_IO_BF16 ? ssm::Io::BF16 : ssm::Io::F32, &w))
+    return -1;
+  return w.floats * 4;
+}
+
 int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
                  const void* C, const float* D, const void* z, const float* delta_bias,
                  const uint8_t* mask, uint32_t flags, const float* chunk_states, const void* dout,
                  const float* dfinal, void* du, void* ddelta, float* dA, float* dB, float* dC,
-                 float* dD, void* dz, float* dbias, float* dh0, int64_t batch, int64_t dim,
-                 int64_t dstate, int64_t seqlen, void* stream) {
+                 float* dD, void* dz, float* dbias, float* dh0, void* workspace,
+                 int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
+                 int64_t seqlen, void* stream) {
   const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
   if (flags & ~known) return SSM_ERR_INVALID_ARG;
   if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return SSM_ERR_INVALID_ARG;
@@ -216,8 +229,30 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
       (delta_bias && !aligned(delta_bias, 4)) || !aligned(chunk_states, 4) ||
       (dfinal && !aligned(dfinal, 4)) || !aligned(dA, 4) || !aligned(dB, 4) ||
       !aligned(dC, 4) || (dD && !aligned(dD, 4)) || (dbias && !aligned(dbias, 4)) ||
-      (dh0 && !aligned(dh0, 4)))
+      (dh0 && !aligned(dh0, 4)) || (workspace && !aligned(workspace, 256)))
     return SSM_ERR_MISALIGNED;
+  if (workspace) {
+    const int64_t need = ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, flags);
+    if (need < 0) return SSM_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return SSM_ERR_INVALID_ARG;
+    // The partial sums are written while the inputs are read and read while the summed
+    // gradients are written: the workspace must overlap no other array.
+    const int64_t eb = elems * esz, bcb = bc * 4, sb = state * 4, ab = a_elems * 4;
+    const Range w = span(workspace, need);
+    // an array that is absent or empty occupies nothing
+    auto sp = [](const void* p, int64_t n) { return (p && n > 0) ? span(p, n) : Range{0, 0}; };
+    const Range others[] = {
+        sp(u, eb), sp(delta, eb), sp(dout, eb), sp(du, eb), sp(ddelta, eb),
+        sp(z, z ? eb : 0), sp(dz, z ? eb : 0), sp(B, bc * esz),
+        sp(C, bc * esz), sp(dB, bcb), sp(dC, bcb), sp(A, ab), sp(dA, ab),
+        sp(D, D ? dim * 4 : 0), sp(dD, (D && dD) ? dim * 4 : 0),
+        sp(delta_bias, delta_bias ? dim * 4 : 0),
+        sp(dbias, (delta_bias && dbias) ? dim * 4 : 0), sp(dfinal, dfinal ? sb : 0),
+        sp(dh0, dh0 ? sb : 0), sp(mask, mask ? batch * seqlen : 0),
+        sp(chunk_states, sb * ssm_scan_ckpt_count(seqlen))};
+    for (const Range& r : others)
+      if (overlaps(w, r)) return SSM_ERR_INVALID_ARG;
+  }
 
   if (rows == 0 && bc == 0 && a_elems == 0) return SSM_OK;
   if (seqlen == 0) {
@@ -265,6 +300,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.dbias = delta_bias ? dbias : nullptr;
   a.dh0 = dh0;
   a.mask = mask;
+  a.workspace = static_cast<float*>(workspace);
   a.batch = batch;
   a.dim = dim;
   a.dstate = dstate;

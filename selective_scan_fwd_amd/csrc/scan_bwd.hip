@@ -15,7 +15,8 @@
 // scans those operators from lane 63 down to lane 0, and each lane replays its steps with
 // the adjoint entering from its right, forming per step:
 //   dC_t += dy_t h_t,  dB_t += g_t s_t u_t  (summed over the workgroup's channels in LDS,
-//   then over workgroups with float atomics), du_t += g_t s_t B_t,
+//   then over workgroups: partial sums in a workspace added up in a fixed order by a second
+//   launch, or float atomics when there is no workspace), du_t += g_t s_t B_t,
 //   ds_t += g_t (A a_t h_{t-1} + B_t u_t), dA += g_t a_t s_t h_{t-1}.
 // The mapping is the forward's: a workgroup owns K channels of one batch row, one
 // wavefront per channel, and lane i owns T consecutive steps of a 64*T-step interval; the
@@ -53,6 +54,11 @@ struct BParams {
   float* dh0;
   const uint8_t* mask;
   int dim, dstate, seqlen, dblocks, softplus, n_ckpt;
+  // 0: dA, dB, dC, dD and dbias are the outputs, summed into with float atomics. 1: they
+  // point into a workspace, where the kernel stores partial sums with plain stores (dB at
+  // [workgroup][dB, dC][state][step], dC unused; dA at [row][state]; dD and dbias at [row])
+  // for bwd_reduce_kernel to add up.
+  int partials;
 };
 
 // Inclusive scan from the right: lane i ends with the composition of the operators of
@@ -182,6 +188,11 @@ __global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
   }
   const float a2_l = A_l * kLog2e;
   float dD_acc = 0.0f, db_acc = 0.0f;
+  // Where the flush adds this workgroup's dB and dC rows: this batch row of the outputs, or
+  // this workgroup's slot of partial sums. Both take the same offset (state, step) after it.
+  const int64_t nl = int64_t(N) * L;
+  float* const flush0 = p.partials ? p.dB + int64_t(blockIdx.x) * 2 * nl : p.dB + b * nl;
+  float* const flush1 = p.partials ? flush0 + nl : p.dC + b * nl;
 
   {
     // rows of inactive waves are read by the flush: they stay zero
@@ -322,7 +333,13 @@ __global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
           float v = 0.0f;
 #pragma unroll 4  // fully unrolled, the K loads in flight would push past 128 registers
           for (int k = 0; k < K; ++k) v += acc[par][wc][k][j * kPitch + ln];
-          if (t < L) unsafeAtomicAdd(&(wc ? p.dC : p.dB)[(int64_t(b) * N + n) * L + t], v);
+          if (t < L) {
+            float* dst = (wc ? flush1 : flush0) + (int64_t(n) * L + t);
+            if (p.partials)
+              *dst = v;
+            else
+              unsafeAtomicAdd(dst, v);
+          }
         }
         ++it;
       }
@@ -372,12 +389,111 @@ __global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
   if (active) {
     if (lane < N) {
       if (p.dh0) p.dh0[row * N + lane] = gc_l;  // e_{-1} = a_0 g_0
-      unsafeAtomicAdd(&p.dA[int64_t(d) * N + lane], dA_l);
+      if (p.partials)
+        p.dA[row * N + lane] = dA_l;
+      else
+        unsafeAtomicAdd(&p.dA[int64_t(d) * N + lane], dA_l);
     }
     const float sD = wave_sum(dD_acc), sb = wave_sum(db_acc);
     if (lane == 0) {
-      if (p.dD) unsafeAtomicAdd(&p.dD[d], sD);
-      if (p.dbias) unsafeAtomicAdd(&p.dbias[d], sb);
+      if (p.partials) {
+        if (p.dD) p.dD[row] = sD;
+        if (p.dbias) p.dbias[row] = sb;
+      } else {
+        if (p.dD) unsafeAtomicAdd(&p.dD[d], sD);
+        if (p.dbias) unsafeAtomicAdd(&p.dbias[d], sb);
+      }
+    }
+  }
+}
+
+// The second launch of a backward with a workspace: every summed gradient is the sum of its
+// partials in a fixed order (no atomics). grid.y = 0: dB and dC, element (b, n, t) summed
+// over the batch row's workgroups; grid.y = 1: dA, dD and dbias summed over batch rows.
+struct RParams {
+  const float* part;
+  const float* part_dA;
+  const float* part_dD;
+  const float* part_dbias;
+  float* dB;
+  float* dC;
+  float* dA;
+  float* dD;      // nullable
+  float* dbias;   // nullable
+  int64_t batch, dim, dstate, seqlen, groups;
+};
+
+// The workgroups g of a batch row are split into kSlices runs of consecutive g; eight
+// threads take one (float, or four neighbouring floats with V = 4) column, one run each, and
+// the runs' sums are added through LDS in run order. Within a run, s_k adds the partials of
+// g = k (mod 4) in increasing g, the tail joins s_0, and the run sum is (s_0 + s_1) +
+// (s_2 + s_3): a fixed order for every element, whatever V is, with 16 loads per thread.
+constexpr int kSlices = 8;
+constexpr int kColumns = 256 / kSlices;
+
+// V = 4 needs dstate * seqlen % 4 == 0 and 16-byte aligned dB and dC.
+template <int V>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(RParams r) {
+  typedef float vec_t __attribute__((ext_vector_type(V)));
+  if (blockIdx.y == 0) {
+    __shared__ vec_t runs[kSlices][kColumns];
+    const int col = threadIdx.x % kColumns, slice = threadIdx.x / kColumns;
+    const int64_t nl = r.dstate * r.seqlen;
+    const int64_t cols = r.batch * 2 * nl / V;
+    const int64_t gs = 2 * nl / V;  // vectors from one workgroup's partials to the next
+    const int64_t per = (r.groups + kSlices - 1) / kSlices;
+    const int64_t g0 = slice * per, g1 = g0 + per < r.groups ? g0 + per : r.groups;
+    for (int64_t base = int64_t(blockIdx.x) * kColumns; base < cols;
+         base += int64_t(gridDim.x) * kColumns) {  // the same trip count for the whole block
+      const int64_t i = base + col;
+      const int64_t bw = (i * V) / nl, e = i * V - bw * nl;  // bw = 2 b + (0: dB, 1: dC)
+      const int64_t b = bw >> 1;
+      vec_t run = 0.0f;
+      if (i < cols) {
+        const vec_t* src =
+            reinterpret_cast<const vec_t*>(r.part + (b * r.groups * 2 + (bw & 1)) * nl + e);
+        vec_t s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+        int64_t g = g0;
+#pragma unroll 4
+        for (; g + 4 <= g1; g += 4) {
+          s0 += src[g * gs];
+          s1 += src[(g + 1) * gs];
+          s2 += src[(g + 2) * gs];
+          s3 += src[(g + 3) * gs];
+        }
+        for (; g < g1; ++g) s0 += src[g * gs];
+        run = (s0 + s1) + (s2 + s3);
+      }
+      runs[slice][col] = run;
+      __syncthreads();
+      if (slice == 0 && i < cols) {
+        vec_t sum = runs[0][col];
+#pragma unroll
+        for (int k = 1; k < kSlices; ++k) sum += runs[k][col];
+        *reinterpret_cast<vec_t*>(((bw & 1) ? r.dC : r.dB) + b * nl + e) = sum;
+      }
+      __syncthreads();
+    }
+  } else {
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    const int64_t first = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t na = r.dim * r.dstate;
+    const int64_t items = na + 2 * r.dim;
+    for (int64_t i = first; i < items; i += stride) {
+      const float* src;
+      float* dst;
+      int64_t e, gs;
+      if (i < na) {
+        src = r.part_dA; dst = r.dA; e = i; gs = na;
+      } else if (i < na + r.dim) {
+        src = r.part_dD; dst = r.dD; e = i - na; gs = r.dim;
+      } else {
+        src = r.part_dbias; dst = r.dbias; e = i - na - r.dim; gs = r.dim;
+      }
+      if (!dst) continue;
+      float s = 0.0f;
+      for (int64_t b = 0; b < r.batch; ++b) s += src[b * gs + e];
+      dst[e] = s;
     }
   }
 }
@@ -425,6 +541,17 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   p.dblocks = int((a.dim + K - 1) / K);
   p.softplus = a.softplus ? 1 : 0;
   p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
+  BwdWorkspace ws{};
+  p.partials = a.workspace ? 1 : 0;
+  if (a.workspace) {
+    if (!bwd_workspace(a.batch, a.dim, a.dstate, a.seqlen, a.io, &ws) || ws.groups != p.dblocks)
+      return int(hipErrorInvalidValue);
+    p.dB = a.workspace + ws.part;
+    p.dC = nullptr;
+    p.dA = a.workspace + ws.dA;
+    p.dD = a.dD ? a.workspace + ws.dD : nullptr;
+    p.dbias = a.dbias ? a.workspace + ws.dbias : nullptr;
+  }
   const int64_t blocks = a.batch * p.dblocks;
   const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * K);
   if (a.vec_ok) {
@@ -438,6 +565,32 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
     else
       hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, false, false>), grid, block, 0, s, p);
   }
+  int st = int(hipGetLastError());
+  if (st != 0 || !a.workspace) return st;
+  RParams r;
+  r.part = a.workspace + ws.part;
+  r.part_dA = a.workspace + ws.dA;
+  r.part_dD = a.workspace + ws.dD;
+  r.part_dbias = a.workspace + ws.dbias;
+  r.dB = a.dB;
+  r.dC = a.dC;
+  r.dA = a.dA;
+  r.dD = a.dD;        // the C-ABI layer has already cleared it when D is absent
+  r.dbias = a.dbias;  // likewise for delta_bias
+  r.batch = a.batch;
+  r.dim = a.dim;
+  r.dstate = a.dstate;
+  r.seqlen = a.seqlen;
+  r.groups = ws.groups;
+  const bool v4 = (a.dstate * a.seqlen) % 4 == 0 && reinterpret_cast<uintptr_t>(a.dB) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(a.dC) % 16 == 0;
+  const int64_t cols = a.batch * 2 * a.dstate * a.seqlen / (v4 ? 4 : 1);
+  int64_t gx = (cols + kColumns - 1) / kColumns;
+  gx = gx < 1 ? 1 : (gx > 16384 ? 16384 : gx);
+  if (v4)
+    hipLaunchKernelGGL(bwd_reduce_kernel<4>, dim3(unsigned(gx), 2), dim3(256), 0, s, r);
+  else
+    hipLaunchKernelGGL(bwd_reduce_kernel<1>, dim3(unsigned(gx), 2), dim3(256), 0, s, r);
   return int(hipGetLastError());
 }
 
@@ -445,8 +598,12 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
 
 int launch_scan_bwd(const BwdArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The channel- and batch-summed gradients are accumulated with atomics: zero all five in
-  // one launch (five small launches cost more than their bytes).
+  if (a.workspace) {  // partial sums, then the reduction launch overwrites every output
+    if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, kBwdChannelsBf16>(a, s);
+    return launch_bwd_typed<float, 8, kBwdChannelsF32>(a, s);
+  }
+  // Without a workspace the channel- and batch-summed gradients are accumulated with
+  // atomics: zero all five in one launch (five small launches cost more than their bytes).
   ZeroList z;
   z.p[0] = a.dA;
   z.n[0] = a.dim * a.dstate;
@@ -470,8 +627,8 @@ int launch_scan_bwd(const BwdArgs& a, void* stream) {
   // bf16: 16 channels per workgroup, half the dB/dC atomics of 8 at the same 4 waves per SIMD
   // (one 16-wave workgroup per CU; its per-wave rows take 144 KB of LDS). fp32 keeps 8: at
   // 16 its masked kernel spills past 128 registers.
-  if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, 16>(a, s);
-  return launch_bwd_typed<float, 8, 8>(a, s);
+  if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, kBwdChannelsBf16>(a, s);
+  return launch_bwd_typed<float, 8, kBwdChannelsF32>(a, s);
 }
 
 }  // namespace ssm

@@ -69,11 +69,53 @@ struct BwdArgs {
   float* dbias;          // nullable
   float* dh0;            // nullable
   const uint8_t* mask;   // nullable: [batch, seqlen], 0 = padding step
+  float* workspace;      // nullable: per-workgroup partial sums (BwdWorkspace); NULL = atomics
   int64_t batch, dim, dstate, seqlen;
   Io io;
   bool softplus;
   bool vec_ok;
 };
+
+// Channels (wavefronts) per backward workgroup, by storage type.
+constexpr int kBwdChannelsBf16 = 16;
+constexpr int kBwdChannelsF32 = 8;
+
+// The backward's workspace, in floats from its start, every region 256-byte aligned:
+//   part  [batch][groups][2][dstate][seqlen]  each workgroup's sums of dB (0) and dC (1)
+//                                             over its channels, groups = ceil(dim / K)
+//   dA    [batch][dim][dstate]                each batch row's dA
+//   dD    [batch][dim]                        each batch row's dD
+//   dbias [batch][dim]                        each batch row's dbias
+// A second launch sums these in a fixed order, so every gradient is reproducible.
+struct BwdWorkspace {
+  int64_t groups;
+  int64_t part, dA, dD, dbias;  // offsets in floats
+  int64_t floats;               // total size in floats
+};
+
+// false on overflow of int64 sizes.
+inline bool bwd_workspace(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, Io io,
+                          BwdWorkspace* w) {
+  const int64_t k = io == Io::BF16 ? kBwdChannelsBf16 : kBwdChannelsF32;
+  const int64_t lim = int64_t(1) << 60;
+  auto mul = [&](int64_t x, int64_t y, int64_t* r) {
+    if (x < 0 || y < 0 || (y != 0 && x > lim / y)) return false;
+    *r = x * y;
+    return true;
+  };
+  auto round64 = [](int64_t x) { return (x + 63) / 64 * 64; };  // 256 bytes of floats
+  int64_t part, rows, rn;
+  w->groups = (dim + k - 1) / k;
+  if (!mul(batch, w->groups, &part) || !mul(part, 2 * dstate, &part) ||
+      !mul(part, seqlen, &part) || !mul(batch, dim, &rows) || !mul(rows, dstate, &rn))
+    return false;
+  w->part = 0;
+  w->dA = round64(part);
+  w->dD = w->dA + round64(rn);
+  w->dbias = w->dD + round64(rows);
+  w->floats = w->dbias + round64(rows);
+  return w->floats < lim;
+}
 
 int launch_scan_bwd(const BwdArgs& a, void* stream);
 

@@ -60,7 +60,7 @@ def test_header_constants_match_binding():
 
 
 def test_abi_version_and_strerror():
-    assert ssm.ssm_scan_abi_version() == 2
+    assert ssm.ssm_scan_abi_version() == 3
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(ssm.ssm_scan_strerror(s), str) and ssm.ssm_scan_strerror(s)
 
@@ -126,6 +126,57 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError):
         ssm.scan(x, x, torch.zeros(2, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
+
+
+# ---------------------------------------------------------------- backward entry
+DOUT, DU, DDL, DA, DB, DC, DH0, CK, BWS = (0x3000000 + 0x100000 * i for i in range(9))
+
+
+def bwd_call(**kw):
+    args = dict(u=U, delta=DL, A=A, B=B, C=C, D=None, z=None, delta_bias=None, mask=None,
+                flags=ssm.SSM_IO_BF16, chunk_states=CK, dout=DOUT, dfinal=None, du=DU,
+                ddelta=DDL, dA=DA, dB=DB, dC=DC, dD=None, dz=None, dbias=None, dh0=DH0,
+                workspace=BWS, workspace_bytes=1 << 20, batch=2, dim=4, dstate=16, seqlen=8,
+                stream=None)
+    args.update(kw)
+    return ssm.ssm_scan_bwd(**args)
+
+
+def test_bwd_workspace_size():
+    # bf16: 16 channels per workgroup; fp32: 8. Regions rounded up to 64 floats.
+    r64 = lambda x: (x + 63) // 64 * 64
+    for flags, k in ((ssm.SSM_IO_BF16, 16), (ssm.SSM_IO_F32, 8)):
+        b, d, n, L = 2, 40, 16, 100
+        groups = (d + k - 1) // k
+        want = 4 * (r64(b * groups * 2 * n * L) + r64(b * d * n) + 2 * r64(b * d))
+        assert ssm.ssm_scan_bwd_workspace_bytes(b, d, n, L, flags) == want
+    assert ssm.ssm_scan_bwd_workspace_bytes(4, 2048, 16, 2048, ssm.SSM_IO_BF16) == \
+        4 * (4 * 128 * 2 * 16 * 2048 + 4 * 2048 * 16 + 2 * 4 * 2048)
+    assert ssm.ssm_scan_bwd_workspace_bytes(0, 4, 16, 8, ssm.SSM_IO_BF16) == 0
+    assert ssm.ssm_scan_bwd_workspace_bytes(-1, 4, 16, 8, ssm.SSM_IO_BF16) == -1
+    assert ssm.ssm_scan_bwd_workspace_bytes(1, 4, 16, 8, 2) == -1
+    assert ssm.ssm_scan_bwd_workspace_bytes(1 << 40, 1 << 20, 64, 1 << 20, 0) == -1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(workspace_bytes=1000),                      # too small
+    dict(workspace=U), dict(workspace=DB - 256),     # overlaps an input / an output
+    dict(workspace=CK), dict(workspace=DH0 + 256),
+    dict(u=None), dict(dB=None), dict(chunk_states=None), dict(flags=1 << 9),
+])
+def test_bwd_invalid_arguments(kw):
+    assert bwd_call(**kw) == ssm.SSM_ERR_INVALID_ARG
+
+
+def test_bwd_misaligned_and_unsupported():
+    assert bwd_call(workspace=BWS + 16) == ssm.SSM_ERR_MISALIGNED
+    assert bwd_call(dstate=65) == ssm.SSM_ERR_UNSUPPORTED
+    assert bwd_call(flags=3) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_bwd_empty_is_a_noop():
+    # no channel, no B/C element and no A entry: nothing to write, no HIP call
+    assert bwd_call(batch=0, dim=0) == ssm.SSM_OK
 
 
 # ---------------------------------------------------------------- Mamba-2 (SSD) entry

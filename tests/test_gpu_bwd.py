@@ -6,8 +6,10 @@ Bar, per tensor (the metric of ssm_workloads.compare, max |g - r| / (|r| + rms(r
     to bf16 on store, as for out);
   * dA, dB, dC, dD, dbias, dh0 and the saved states (always float32): 1e-4, which leaves
     about two orders of magnitude over the float32 rounding of sums of up to ~1e4 terms.
-The channel- and batch-summed gradients use float atomics, so only du, ddelta, dz and dh0
-are compared bit for bit between runs.
+By default the channel- and batch-summed gradients (dA, dB, dC, dD, dbias) go through the
+workspace path (per-workgroup partial sums added in a fixed order), so every gradient is
+compared bit for bit between runs; the float-atomic path (no workspace) is checked against
+the oracle too, and against the workspace path within float32 rounding.
 """
 import numpy as np
 import pytest
@@ -45,7 +47,7 @@ def setup(w, softplus=True, use_D=True, use_z=True, use_bias=True, dfinal=True, 
     return inp, dout, dfin
 
 
-def run_gpu(inp, dout, dfin, softplus):
+def run_gpu(inp, dout, dfin, softplus, deterministic=True, workspace=None):
     io = inp["io"]
     g = {k: dev(inp[k], io) for k in ("u", "delta", "B", "C", "z")}
     f = {k: dev(inp[k], "f32") for k in ("A", "D", "delta_bias", "h0")}
@@ -55,7 +57,8 @@ def run_gpu(inp, dout, dfin, softplus):
     grads = ssm.scan_backward(g["u"], g["delta"], f["A"], g["B"], g["C"], states,
                               dev(dout, io), D=f["D"], z=g["z"], delta_bias=f["delta_bias"],
                               delta_softplus=softplus,
-                              dfinal=None if dfin is None else dev(dfin, "f32"))
+                              dfinal=None if dfin is None else dev(dfin, "f32"),
+                              deterministic=deterministic, workspace=workspace)
     torch().cuda.synchronize()
     res = {k: (None if v is None else host(v)) for k, v in grads.items()}
     return host(out), host(fin), host(states), res
@@ -146,15 +149,72 @@ def test_saved_states_and_forward_unchanged(io):
         assert rep.ok, f"state {k}: {rep}"
 
 
+ALL_GRADS = ("du", "ddelta", "dz", "dh0", "dA", "dB", "dC", "dD", "dbias")
+
+
 def test_backward_per_element_outputs_are_deterministic():
+    """Atomic path: the per-element gradients and dh0 are still reproducible."""
     w = WORKLOADS["tiny"].with_(batch=2, dim=16, dstate=16, seqlen=1100, io="bf16", gate=True,
                                 initial_state=True, seed=64)
-    announce(w.describe() + " determinism")
+    announce(w.describe() + " determinism (atomics)")
     inp, dout, dfin = setup(w, seed=64)
-    *_, g1 = run_gpu(inp, dout, dfin, True)
-    *_, g2 = run_gpu(inp, dout, dfin, True)
+    *_, g1 = run_gpu(inp, dout, dfin, True, deterministic=False)
+    *_, g2 = run_gpu(inp, dout, dfin, True, deterministic=False)
     for k in ("du", "ddelta", "dz", "dh0"):
         assert np.array_equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_workspace_sums_are_reproducible(io):
+    """Workspace path: every gradient, the summed ones included, is bitwise the same from
+    run to run (several workgroups per batch row, a ragged channel count and tail)."""
+    w = WORKLOADS["tiny"].with_(batch=3, dim=37, dstate=16, seqlen=1300, io=io, gate=True,
+                                initial_state=True, seed=66)
+    announce(w.describe() + " determinism (workspace)")
+    inp, dout, dfin = setup(w, seed=66)
+    *_, g1 = run_gpu(inp, dout, dfin, True)
+    *_, g2 = run_gpu(inp, dout, dfin, True)
+    for k in ALL_GRADS:
+        assert np.array_equal(g1[k], g2[k]), k
+    compare(io, g1, run_oracle(inp, dout, dfin, True), w.describe())
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 9, 16, 100), (1, 4, 17, 2049), (2, 37, 64, 600)],
+                         ids=lambda s: "b{}d{}N{}L{}".format(*s))
+def test_backward_atomic_path(shape, io):
+    """The float-atomic path (no workspace) against the oracle."""
+    b, d, n, L = shape
+    w = WORKLOADS["tiny"].with_(batch=b, dim=d, dstate=n, seqlen=L, io=io, gate=True,
+                                initial_state=True, a_kind="scaled", seed=700 + L + n)
+    announce(w.describe() + " backward (atomics)")
+    inp, dout, dfin = setup(w, seed=L + 1)
+    *_, got = run_gpu(inp, dout, dfin, True, deterministic=False)
+    compare(io, got, run_oracle(inp, dout, dfin, True), w.describe() + " atomics")
+
+
+def test_backward_workspace_reused_and_paths_agree():
+    """One caller-held workspace, larger than needed, serves two different problems in a
+    row; on the same problem the two summation paths agree within float32 rounding and the
+    per-element gradients are identical."""
+    t = torch()
+    need = max(ssm.ssm_scan_bwd_workspace_bytes(2, 40, 16, 900, ssm.SSM_IO_BF16),
+               ssm.ssm_scan_bwd_workspace_bytes(1, 24, 8, 1500, ssm.SSM_IO_BF16))
+    ws = t.full((need + 4096,), 0x7F, dtype=t.uint8, device="cuda")  # stale contents
+    for i, (b, d, n, L) in enumerate([(2, 40, 16, 900), (1, 24, 8, 1500)]):
+        w = WORKLOADS["tiny"].with_(batch=b, dim=d, dstate=n, seqlen=L, io="bf16", gate=True,
+                                    initial_state=True, seed=67 + i)
+        announce(w.describe() + " workspace reuse")
+        inp, dout, dfin = setup(w, seed=67 + i)
+        *_, gw = run_gpu(inp, dout, dfin, True, workspace=ws)
+        compare("bf16", gw, run_oracle(inp, dout, dfin, True), w.describe() + " reused ws")
+        *_, ga = run_gpu(inp, dout, dfin, True, deterministic=False)
+        for k in ("du", "ddelta", "dz", "dh0"):
+            assert np.array_equal(gw[k], ga[k]), k
+        for k in ("dA", "dB", "dC", "dD", "dbias"):
+            rep = parity(ga[k], gw[k].astype(np.float64), 1e-5)
+            print(f"[paths] {k}: {rep}", flush=True)
+            assert rep.ok, f"{k}: {rep}"
 
 
 def test_backward_layer_workload_full():
