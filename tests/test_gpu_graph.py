@@ -11,7 +11,9 @@ results are reproducible), and the eager results against the float64 oracle.
 Cases: a decode loop of one-token calls carrying the state in place (the state cache of
 ybb.press/ai-applications/14118.html section 5.1, one call per generated token), the
 chunked forward at a layer-like shape with new inputs written into the captured buffers
-between replays, and the Mamba-2 (SSD) forward with a caller-held workspace.
+between replays, the Mamba-2 (SSD) forward with a caller-held workspace, and a training
+step (forward with saved states, then the backward with its workspace, whose fixed-order
+sums make every gradient bitwise reproducible).
 """
 import numpy as np
 import pytest
@@ -187,3 +189,51 @@ def test_graph_ssd_forward():
         t.cuda.synchronize()
         assert same(out, e_out) and same(fin, e_fin), f"replay {r} differs from eager"
         print(f"[graph] ssd replay {r}: bitwise equal to eager", flush=True)
+
+
+def test_graph_training_step():
+    """ssm_scan_fwd_ckpt then ssm_scan_bwd (workspace path) captured as one graph: every
+    replay's outputs, saved states and gradients equal the eager step's bit for bit."""
+    t = torch()
+    w = WORKLOADS["layer"].with_(batch=2, dim=96, seqlen=1300, initial_state=True, seed=504)
+    announce(f"{w.describe()} graph training step")
+    inp = make_inputs(w)
+    g = {k: dev(inp[k], w.io) for k in ("u", "delta", "B", "C", "z")}
+    f = {k: dev(inp[k], "f32") for k in ("A", "D", "delta_bias", "h0")}
+    gen = t.Generator(device="cuda")
+    gen.manual_seed(505)
+    dout = t.randn(g["u"].shape, device="cuda", generator=gen).to(g["u"].dtype)
+    dfinal = t.randn((w.batch, w.dim, w.dstate), device="cuda", generator=gen)
+    flags = ssm.SSM_IO_BF16 | ssm.SSM_DELTA_SOFTPLUS
+    ws = t.empty(ssm.ssm_scan_bwd_workspace_bytes(w.batch, w.dim, w.dstate, w.seqlen, flags),
+                 dtype=t.uint8, device="cuda")
+
+    def step():
+        out, fin, states = ssm.scan_train(g["u"], g["delta"], f["A"], g["B"], g["C"], D=f["D"],
+                                          z=g["z"], delta_bias=f["delta_bias"],
+                                          delta_softplus=True, h0=f["h0"])
+        grads = ssm.scan_backward(g["u"], g["delta"], f["A"], g["B"], g["C"], states, dout,
+                                  D=f["D"], z=g["z"], delta_bias=f["delta_bias"],
+                                  delta_softplus=True, dfinal=dfinal, workspace=ws)
+        return {"out": out, "fin": fin, "states": states, **grads}
+
+    eager = {k: v.clone() for k, v in step().items() if v is not None}
+    t.cuda.synchronize()
+    ref = oracle.scan_ref(widen(inp["u"], w.io), widen(inp["delta"], w.io), inp["A"],
+                          widen(inp["B"], w.io), widen(inp["C"], w.io), inp["D"],
+                          widen(inp["z"], w.io), inp["delta_bias"], True, inp["h0"])
+    check(w.io, (host(eager["out"]), host(eager["fin"])), ref, f"{w.describe()} eager step")
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.graph(graph):
+        captured = step()
+    for r in range(REPLAYS):
+        for v in captured.values():
+            if v is not None:
+                v.zero_()
+        ws.zero_()
+        unrelated_eager_work(t)
+        graph.replay()
+        t.cuda.synchronize()
+        for k, v in eager.items():
+            assert same(captured[k], v), f"replay {r}: {k} differs from eager"
+        print(f"[graph] training step replay {r}: bitwise equal to eager", flush=True)
