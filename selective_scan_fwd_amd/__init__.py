@@ -10,6 +10,9 @@ ABI of include/ssm_scan.h. PyTorch supplies device memory and the current stream
                           delta_bias=None, delta_softplus=False, dfinal=None)
     out, final_state = ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None,
                            dt_softplus=False, h0=None, mask=None)      # Mamba-2, ssm_ssd.h
+    out, final_state = selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                                      delta_softplus=False, h0=None, mask=None)
+                       # differentiable: scan_train forward, scan_backward under autograd
 
 The ``ssm_scan_*`` functions are the raw C entry points (pointers as ints). If the
 library has not been built this module raises on first use; there is no CPU fallback.
@@ -339,6 +342,55 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
     if status != SSM_OK:
         raise SsmScanError(status)
     return g
+
+
+_autograd_fn = None
+
+
+def _selective_scan_function():
+    """The torch.autograd.Function behind ``selective_scan`` (built on first use, so that
+    importing this module does not import torch)."""
+    global _autograd_fn
+    if _autograd_fn is not None:
+        return _autograd_fn
+    import torch
+
+    class SelectiveScan(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, mask, delta_softplus):
+            out, fin, states = scan_train(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                                          delta_softplus=delta_softplus, h0=h0, mask=mask)
+            ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, states)
+            ctx.mask = mask
+            ctx.delta_softplus = delta_softplus
+            ctx.has_h0 = h0 is not None
+            return out, fin
+
+        @staticmethod
+        def backward(ctx, dout, dfin):
+            u, delta, A, B, C, D, z, delta_bias, states = ctx.saved_tensors
+            dout = torch.zeros_like(u) if dout is None else dout.to(u.dtype).contiguous()
+            dfin = None if dfin is None else dfin.to(torch.float32).contiguous()
+            g = scan_backward(u, delta, A, B, C, states, dout, D=D, z=z, delta_bias=delta_bias,
+                              delta_softplus=ctx.delta_softplus, dfinal=dfin,
+                              want_dh0=ctx.has_h0 and ctx.needs_input_grad[8], mask=ctx.mask)
+            cast = lambda grad, like: None if grad is None else grad.to(like.dtype)
+            return (g["du"], g["ddelta"], cast(g["dA"], A), cast(g["dB"], B), cast(g["dC"], C),
+                    g["dD"], g["dz"], g["dbias"], g["dh0"], None, None)
+
+    _autograd_fn = SelectiveScan
+    return SelectiveScan
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                   delta_softplus: bool = False, h0=None, mask=None
+                   ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Differentiable selective scan: (out, final_state) as ``scan``, with gradients for u,
+    delta, A, B, C, D, z, delta_bias and h0 through autograd. The forward keeps the state
+    every 512 steps (``scan_train``); the backward restarts the scan from them
+    (``scan_backward``, reproducible workspace sums). mask is not differentiable."""
+    return _selective_scan_function().apply(u, delta, A, B, C, D, z, delta_bias, h0, mask,
+                                            bool(delta_softplus))
 
 
 def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = False, h0=None,
