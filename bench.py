@@ -130,6 +130,13 @@ def cpu_baseline(w, inp, budget_s: float):
     reps = max(1, min(500, int(budget_s / max(timed(nb, nd), 1e-6)))) if rows == total_rows else 1
     secs = sum(timed(nb, nd) for _ in range(reps)) / reps
     sub = w.with_(batch=nb, dim=nd)
+    # the same oracle on one thread, over the first channels of batch row 0 (about a second)
+    one_d = max(1, min(w.dim, int(probe_d * 1.0 / max(t_probe * threads, 1e-6))))
+    one_args = sample(1, one_d)
+    t0 = time.perf_counter()
+    oracle.scan_ref(*one_args, nthreads=1)
+    one_secs = max(time.perf_counter() - t0, 1e-9)
+    one_sub = w.with_(batch=1, dim=one_d)
     return {
         "value": round(sub.algorithmic_bytes() / secs / 1e9, 4),
         "unit": "GB/s",
@@ -140,7 +147,49 @@ def cpu_baseline(w, inp, budget_s: float):
                    f"{sub.algorithmic_bytes() / 1e6:.2f} MB algorithmic), mean of {reps} run(s) "
                    f"of {secs:.2f} s"),
         "seconds": round(secs, 3),
+        "single_thread": {"value": round(one_sub.algorithmic_bytes() / one_secs / 1e9, 4),
+                          "unit": "GB/s",
+                          "sample": f"batch row 0, channels 0..{one_d - 1}, all {w.seqlen} steps",
+                          "seconds": round(one_secs, 3)},
+        "host": host_description(),
     }
+
+
+def host_description():
+    """CPU model and the number of cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def copy_reference(torch) -> dict:
+    """Device copy of 512 MiB (torch's copy kernel; source and destination together exceed
+    the Infinity Cache), median of 10 launches between HIP events: the bandwidth a plain
+    streaming kernel reaches on this GPU."""
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(10)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del src, dst
+    return {"GBps": round(2 * n / (ms * 1e-3) / 1e9, 1), "bytes_read": n, "bytes_written": n,
+            "kernel_us_median": round(ms * 1e3, 2)}
 
 
 def copy_probe(torch, steps: int, warmup: int) -> int:
@@ -751,6 +800,10 @@ def main() -> int:
         "roofline": roofline,
         "warm": warm,
     }
+    copy = copy_reference(torch)
+    copy["pct_of_copy"] = round(100.0 * value / copy["GBps"], 2)
+    copy["note"] = "value against a plain device copy measured in this run, after the metric"
+    result["copy_reference"] = copy
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_baseline_seconds)
     print(json.dumps(result), flush=True)
