@@ -960,6 +960,18 @@ __global__ __launch_bounds__(128 * ChunkLayout<N>::kNS) void ssd_chunk_kernel(Ss
       xl[kb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
 
+    // B (w o x) for the state update. It needs only this block's operands, so it is issued
+    // here, ahead of the output arithmetic, which the matrix cores then overlap.
+    f32x4 T[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        T[jt] = mfma16(bop[kb][jt], xh[kb], T[jt]);
+        T[jt] = mfma16(bop[kb][jt], xl[kb], T[jt]);
+      }
+    }
+
     // Outputs: separable, y = e_t (exp(ref) C^T H + (G o L) (w o x)); otherwise
     // y = e_t C^T H + M x with M[t][s] = G[t][s] exp(cs_t - cs_s) dt_s formed in registers,
     // in the operand layout (lane (r, g): row t, s = 32 kb + 8 g .. + 7).
@@ -1024,16 +1036,7 @@ __global__ __launch_bounds__(128 * ChunkLayout<N>::kNS) void ssd_chunk_kernel(Ss
       store4<kVec>(obuf, xrow, t0 + 16 * i + 4 * g, L, wave_on, y);
     }
 
-    // State: H <- exp(cs_end) H + exp(cs_end - ref) B (w o x).
-    f32x4 T[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        T[j] = mfma16(bop[kb][j], xh[kb], T[j]);
-        T[j] = mfma16(bop[kb][j], xl[kb], T[j]);
-      }
-    }
+    // State: H <- exp(cs_end) H + exp(cs_end - ref) B (w o x), with T = B (w o x) formed above.
     const float alpha = exp2_hw(cs_end * kLog2e);
     const float beta = sep ? exp2_hw((cs_end - ref) * kLog2e) : 1.0f;
 #pragma unroll
