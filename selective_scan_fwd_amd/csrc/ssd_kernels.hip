@@ -730,8 +730,11 @@ struct ChunkLoads {
   float4 w[4];            // w_s, s = 32 kb + 8 g + 4 k .. + 3  (index 2 kb + k)
   float4 e[CL::kOwn];     // e_t at this lane's output rows
   float cse;              // cs_end of the block
-  uint4 bst[kVec ? 1 : CL::kBInstr];   // element-wise path: B and x/z words for the stages
-  uint4 xst[kVec ? 1 : CL::kXZInstr];
+  // Element-wise path: B and x/z words for the stages. The vector path copies straight to
+  // LDS and never touches these (the compiler drops them), but the copy routine still takes
+  // a reference to the slot, so they are sized for its largest index on both paths.
+  uint4 bst[CL::kBInstr];
+  uint4 xst[CL::kXZInstr];
 };
 
 template <int N, bool kVec>
