@@ -14,8 +14,10 @@ ABI of include/ssm_scan.h. PyTorch supplies device memory and the current stream
                                       delta_softplus=False, h0=None, mask=None)
                        # differentiable: scan_train forward, scan_backward under autograd
 
-The ``ssm_scan_*`` functions are the raw C entry points (pointers as ints). If the
-library has not been built this module raises on first use; there is no CPU fallback.
+Inputs may be strided views: the functions above copy them to contiguous tensors first
+(outputs passed in must be contiguous). The ``ssm_scan_*`` functions are the raw C entry
+points (pointers as ints). If the library has not been built this module raises on first
+use; there is no CPU fallback.
 """
 from __future__ import annotations
 
@@ -162,6 +164,12 @@ def _stream_of(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _dense(*tensors):
+    """Inputs as C-contiguous tensors (a strided view, such as a slice of a projection's
+    output, is copied once here; the C ABI takes contiguous arrays only)."""
+    return tuple(t if t is None or t.is_contiguous() else t.contiguous() for t in tensors)
+
+
 def _check(u, delta, A, B, C, D, z, delta_bias, h0):
     """Dtype, device, contiguity and shape checks; returns (flags, batch, dim, dstate, seqlen)."""
     import torch
@@ -216,6 +224,8 @@ def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final
              return_final_state, save_states, mask=None):
     import torch
 
+    u, delta, A, B, C, D, z, delta_bias, h0, mask = _dense(u, delta, A, B, C, D, z, delta_bias,
+                                                           h0, mask)
     flags, batch, dim, dstate, seqlen = _check(u, delta, A, B, C, D, z, delta_bias, h0)
     mask = _check_mask(mask, u, batch, seqlen)
     io = u.dtype
@@ -294,6 +304,8 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
     atomics, no workspace."""
     import torch
 
+    u, delta, A, B, C, D, z, delta_bias, mask, chunk_states, dout, dfinal = _dense(
+        u, delta, A, B, C, D, z, delta_bias, mask, chunk_states, dout, dfinal)
     flags, batch, dim, dstate, seqlen = _check(u, delta, A, B, C, D, z, delta_bias, None)
     mask = _check_mask(mask, u, batch, seqlen)
     n_ck = ssm_scan_ckpt_count(seqlen)
@@ -407,6 +419,7 @@ def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = False,
     """
     import torch
 
+    x, dt, A, B, C, D, z, dt_bias, h0, mask = _dense(x, dt, A, B, C, D, z, dt_bias, h0, mask)
     if x.dtype != torch.bfloat16:
         raise TypeError("ssd takes bfloat16 x, dt, B, C and z")
     if x.dim() != 3 or A.dim() != 1:

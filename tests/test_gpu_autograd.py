@@ -89,3 +89,32 @@ def test_autograd_partial_inputs_and_outputs():
     for k in ("delta", "B", "C", "D", "z", "delta_bias", "h0"):
         assert x[k].grad is None, k
     assert np.isfinite(x["u"].grad.float().cpu().numpy()).all()
+
+
+def test_strided_inputs_are_copied():
+    """Strided views (B and C as slices of a [batch, seqlen, 2N] projection, u transposed)
+    give bitwise the same results as contiguous copies, through scan, selective_scan and
+    scan_backward."""
+    t = torch()
+    w = WORKLOADS["tiny"].with_(batch=2, dim=12, dstate=16, seqlen=300, io="bf16", gate=True,
+                                initial_state=True, seed=84)
+    announce(f"{w.describe()} strided inputs")
+    inp = make_inputs(w)
+    x = leaves(inp, "bf16", requires=())
+    proj = t.cat([x["B"].transpose(1, 2), x["C"].transpose(1, 2)], dim=2).contiguous()
+    Bv, Cv = proj[..., :w.dstate].transpose(1, 2), proj[..., w.dstate:].transpose(1, 2)
+    uv = x["u"].transpose(1, 2).contiguous().transpose(1, 2)
+    assert not (Bv.is_contiguous() or Cv.is_contiguous() or uv.is_contiguous())
+    kw = dict(D=x["D"], z=x["z"], delta_bias=x["delta_bias"], delta_softplus=True, h0=x["h0"])
+    o1, f1 = ssm.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], **kw)
+    o2, f2 = ssm.scan(uv, x["delta"], x["A"], Bv, Cv, **kw)
+    assert same(o1, o2) and same(f1, f2)
+    _, _, st = ssm.scan_train(x["u"], x["delta"], x["A"], x["B"], x["C"], **kw)
+    dout = t.ones_like(o1)
+    kb = dict(D=x["D"], z=x["z"], delta_bias=x["delta_bias"], delta_softplus=True)
+    g1 = ssm.scan_backward(x["u"], x["delta"], x["A"], x["B"], x["C"], st, dout, **kb)
+    g2 = ssm.scan_backward(uv, x["delta"], x["A"], Bv, Cv, st, dout.transpose(1, 2).contiguous()
+                           .transpose(1, 2), **kb)
+    for k, v in g1.items():
+        if v is not None:
+            assert same(v, g2[k]), k
