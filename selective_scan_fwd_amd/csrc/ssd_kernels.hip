@@ -243,18 +243,32 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p, int n_prep, 
   const uint32_t bc_bytes = uint32_t(N) * uint32_t(L) * 2u;
   const Buf cbuf(p.C + size_t(b) * N * L, bc_bytes), bbuf(p.B + size_t(b) * N * L, bc_bytes);
 
-  // Transpose the block's B and C into LDS: thread -> (state n, 8 steps).
-  for (int idx = threadIdx.x; idx < N * 8; idx += 256) {
-    const int n = idx >> 3, q = idx & 7;
-    const uint4 wc = load8<kVec>(cbuf, uint32_t(n) * L, t0 + 8 * q, L);
-    const uint4 wb = load8<kVec>(bbuf, uint32_t(n) * L, t0 + 8 * q, L);
-    const uint32_t vc[4] = {wc.x, wc.y, wc.z, wc.w}, vb[4] = {wb.x, wb.y, wb.z, wb.w};
+  // Transpose the block's B and C into LDS: thread -> (states n, n + 1; steps 8 q .. + 7).
+  // Each step's two states go in as one 32-bit write, and consecutive lanes take
+  // consecutive state pairs, so one write instruction covers consecutive words of one row:
+  // no bank conflicts. (Lanes on the same state pair would write rows 8 apart, 2 176 bytes,
+  // all on one bank.) The 16-byte loads then come from different rows; the other step
+  // groups of each 128-byte row are read by the neighbouring waves, from L2.
+  for (int idx = threadIdx.x; idx < N * 4; idx += 256) {
+    const int n = 2 * (idx % (N / 2)), q = idx / (N / 2);
+    const uint4 c0 = load8<kVec>(cbuf, uint32_t(n) * L, t0 + 8 * q, L);
+    const uint4 c1 = load8<kVec>(cbuf, uint32_t(n + 1) * L, t0 + 8 * q, L);
+    const uint4 b0 = load8<kVec>(bbuf, uint32_t(n) * L, t0 + 8 * q, L);
+    const uint4 b1 = load8<kVec>(bbuf, uint32_t(n + 1) * L, t0 + 8 * q, L);
+    const uint32_t vc0[4] = {c0.x, c0.y, c0.z, c0.w}, vc1[4] = {c1.x, c1.y, c1.z, c1.w};
+    const uint32_t vb0[4] = {b0.x, b0.y, b0.z, b0.w}, vb1[4] = {b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      ct[8 * q + 2 * k][n] = uint16_t(vc[k]);
-      ct[8 * q + 2 * k + 1][n] = uint16_t(vc[k] >> 16);
-      bt[8 * q + 2 * k][n] = uint16_t(vb[k]);
-      bt[8 * q + 2 * k + 1][n] = uint16_t(vb[k] >> 16);
+      // step 8 q + 2 k: the low halves of state n's and state n + 1's words; step + 1: the
+      // high halves (v_perm_b32 selector bytes: result = {hi-or-lo of src1, of src0})
+      *reinterpret_cast<uint32_t*>(&ct[8 * q + 2 * k][n]) =
+          __builtin_amdgcn_perm(vc1[k], vc0[k], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&ct[8 * q + 2 * k + 1][n]) =
+          __builtin_amdgcn_perm(vc1[k], vc0[k], 0x07060302u);
+      *reinterpret_cast<uint32_t*>(&bt[8 * q + 2 * k][n]) =
+          __builtin_amdgcn_perm(vb1[k], vb0[k], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&bt[8 * q + 2 * k + 1][n]) =
+          __builtin_amdgcn_perm(vb1[k], vb0[k], 0x07060302u);
     }
   }
   __syncthreads();
