@@ -79,34 +79,45 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // kCkpt: also write the saved states of a training forward; kMask: read a padding mask.
 // Each is a separate instantiation, so the plain forward carries neither (its register
 // count decides how many waves fit on a SIMD).
+// S: wavefronts per channel. With S = 2 the two waves of a channel split its states (a stage
+// holds G states for each), both run the per-step work, and at the end of a chunk the second
+// hands its share of y to the first through LDS; for launches with too few channels to give
+// every SIMD two waves. Each wave carries, and saves, the states it scans.
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bool kCkpt,
-          bool kMask>
-__global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
+          bool kMask, int S = 1>
+__global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
   constexpr int kVec = Vec<Elem>::kN;          // elements per 16-byte word
   constexpr int kChunk = 64 * T;               // steps per chunk
   static_assert(kChunk == 2 * kCkptInterval, "checkpoints sit at chunk starts and halves");
   constexpr int kQuads = T / 4;                // float4 LDS words per lane per state
   constexpr int kWordsPerState = kChunk / kVec;      // 16-byte words per state per chunk
-  constexpr int kArrayWords = G * kWordsPerState;    // words per array (B or C) per stage
+  constexpr int kGS = G * S;                   // states per stage (G for each wave of a channel)
+  constexpr int kArrayWords = kGS * kWordsPerState;  // words per array (B or C) per stage
   constexpr int kStageWords = 2 * kArrayWords;       // B words, then C words
-  constexpr int kWordsPerLane = (kStageWords + 64 * K - 1) / (64 * K);
+  constexpr int kThreads = 64 * K * S;
+  constexpr int kWordsPerLane = (kStageWords + kThreads - 1) / kThreads;
   constexpr int kBlocks = T / kVec;            // 16-byte words per lane per chunk
   constexpr uint32_t kEsz = sizeof(Elem);
   constexpr bool kBf16 = kEsz == 2;
   static_assert(T % 8 == 0, "a lane block must hold whole 16-byte bf16 words");
   static_assert(kArrayWords % 64 == 0, "each wavefront stages words of one array only");
   static_assert(!kDmaInputs || kVecRows, "input DMA moves whole aligned 16-byte words");
+  static_assert(S == 1 || S == 2, "one or two waves per channel");
 
   // Staging: [buffer][B=0 / C=1][state-in-group][quad][lane] as float4 (fp32 slots).
-  __shared__ float4 lds_bc[2][2][G * kQuads * 64];
+  __shared__ float4 lds_bc[2][2][kGS * kQuads * 64];
   // Next chunk's u and delta words, per wavefront: [wave][u=0 / delta=1][word][lane].
-  __shared__ uint4 lds_in[kDmaInputs ? K : 1][2][kBlocks][64];
+  __shared__ uint4 lds_in[kDmaInputs ? K * S : 1][2][kBlocks][64];
+  // S = 2: the second wave's share of y at the end of a chunk, [channel][quad][lane].
+  __shared__ float4 lds_y[S == 2 ? K : 1][S == 2 ? kQuads : 1][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = S == 1 ? 0 : wave / K;     // which share of the states this wave scans
+  const int slot = S == 1 ? wave : wave % K;  // its channel within the workgroup
   const int b = blockIdx.x / p.dblocks;
-  const int d = (blockIdx.x - b * p.dblocks) * K + wave;
+  const int d = (blockIdx.x - b * p.dblocks) * K + slot;
   const bool active = d < p.dim;  // a wave past the last channel stages, syncs, stores nothing
   const int N = p.dstate, L = p.seqlen;
   const int64_t row = int64_t(b) * p.dim + (active ? d : 0);
@@ -132,7 +143,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
     }
   }
 
-  const int n_groups = (N + G - 1) / G;
+  const int n_groups = (N + kGS - 1) / kGS;
   const int n_chunks = (L + kChunk - 1) / kChunk;
 
   // ---- B/C staging. Word w of a stage: array w / kArrayWords, state-in-group
@@ -141,11 +152,11 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   int st_a[kWordsPerLane], st_nl[kWordsPerLane], st_s[kWordsPerLane], st_idx[kWordsPerLane];
 #pragma unroll
   for (int k = 0; k < kWordsPerLane; ++k) {
-    const int w = k * 64 * K + tid;
+    const int w = k * kThreads + tid;
     const int wa = w % kArrayWords;
     // w / kArrayWords is the same for the whole wavefront (kArrayWords % 64 == 0)
     st_a[k] = __builtin_amdgcn_readfirstlane(w / kArrayWords);
-    st_nl[k] = (w < kStageWords) ? wa / kWordsPerState : G;  // G: this lane holds no word
+    st_nl[k] = (w < kStageWords) ? wa / kWordsPerState : kGS;  // kGS: this lane holds no word
     st_s[k] = (wa % kWordsPerState) * kVec;
     st_idx[k] = (st_nl[k] * kQuads + (st_s[k] % T) / 4) * 64 + st_s[k] / T;
   }
@@ -155,9 +166,9 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
     const int c = it / n_groups, g = it - c * n_groups;
 #pragma unroll
     for (int k = 0; k < kWordsPerLane; ++k) {
-      const int n = g * G + st_nl[k];
+      const int n = g * kGS + st_nl[k];
       const int t = c * kChunk + st_s[k];
-      const bool ok = st_nl[k] < G && n < N && t < L;
+      const bool ok = st_nl[k] < kGS && n < N && t < L;
       const uint32_t e = ok ? uint32_t(n) * uint32_t(L) + uint32_t(t) : bc_elems;
       raw[k] = load_word<Elem, kVecRows>(st_a[k] == 0 ? B_buf : C_buf, e);
     }
@@ -165,8 +176,8 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   auto stage_commit = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < kWordsPerLane; ++k) {
-      if (st_a[k] < 2 && st_nl[k] < G) {
-        float4* base = &lds_bc[buf][0][0] + st_a[k] * (G * kQuads * 64) + st_idx[k];
+      if (st_a[k] < 2 && st_nl[k] < kGS) {
+        float4* base = &lds_bc[buf][0][0] + st_a[k] * (kGS * kQuads * 64) + st_idx[k];
         if constexpr (kBf16) {
           // bf16 is the top half of an fp32: store each value into the upper 16 bits of its
           // slot; the lower halves were zeroed once and are never written again.
@@ -224,12 +235,13 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
     const int buf = it & 1;
 #pragma unroll
     for (int nl = 0; nl < G; ++nl) {
-      const int n = g * G + nl;
+      const int sl = half * G + nl;  // state within the stage
+      const int n = g * kGS + sl;
       if (n < N) {
         const float a2 = readlane(a2_lane, n);
         const float hc = readlane(hc_lane, n);
-        const float4* Bq = &lds_bc[buf][0][nl * kQuads * 64 + lane];
-        const float4* Cq = &lds_bc[buf][1][nl * kQuads * 64 + lane];
+        const float4* Bq = &lds_bc[buf][0][sl * kQuads * 64 + lane];
+        const float4* Cq = &lds_bc[buf][1][sl * kQuads * 64 + lane];
         // All of this state's B words are requested at once, and its C words before the
         // wave scan, so LDS latency overlaps the exps and the scan.
         float4 bq[kQuads], cq[kQuads];
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
 
   if constexpr (kBf16) {
     float4* flat = &lds_bc[0][0][0];
-    for (int i = tid; i < 2 * 2 * G * kQuads * 64; i += 64 * K)
+    for (int i = tid; i < 2 * 2 * kGS * kQuads * 64; i += kThreads)
       flat[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     __syncthreads();
   }
@@ -287,10 +299,12 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
   stage_commit(0);
   __syncthreads();
 
+  // The states whose carries (and saved states) lane `lane` of this wave holds.
+  const bool own = S == 1 || (lane % kGS) / G == half;
   for (int c = 0; c < n_chunks; ++c) {
     const int tb = c * kChunk + lane * T;
     sdt = 0.0f;
-    if (kCkpt && active && lane < N)  // the state entering the chunk
+    if (kCkpt && active && lane < N && own)  // the state entering the chunk
       p.ckpt[(row * p.n_ckpt + 2 * c) * N + lane] = hc_lane;
     {
       const bool tail = (c + 1) * kChunk > L;
@@ -312,7 +326,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
           const int j = q * kVec + e;
           dt[j] = dr[e] + bias_d;
           du[j] = uv[e];  // u for now; times the step size below
-          y[j] = Dd * uv[e];
+          y[j] = half == 0 ? Dd * uv[e] : 0.0f;  // the D skip once per channel
         }
       }
       // Each flag is tested once per chunk, around whole loops: a test per step would be
@@ -353,7 +367,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
         load_inputs(c + 1);
         asm volatile("" ::: "memory");  // the DMA stays ahead of the z loads below
       }
-      if (g == n_groups - 1) load_z(c);
+      if (g == n_groups - 1 && half == 0) load_z(c);
       if (active) compute_group(it, g);
       stage_commit((it + 1) & 1);
       if constexpr (kDmaInputs) {
@@ -364,7 +378,7 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
         // group every VMEM operation but the z loads issued after it must have completed.
         // Commits are LDS writes, complete before every barrier.
         if (g == n_groups - 1) {
-          if (p.z) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlocks) : "memory");
+          if (p.z && half == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlocks) : "memory");
           else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -373,21 +387,44 @@ __global__ __launch_bounds__(64 * K) void scan_fwd_kernel(KParams p) {
       }
     }
 
-    if (p.z) {
+    if constexpr (S == 2) {
+      // The second wave's share of y joins the first's; the first then gates and stores.
+      // lds_y is written again only at the end of the next chunk, after at least one more
+      // barrier, by which time the first wave has read it.
+      if (half == 1) {
 #pragma unroll
-      for (int q = 0; q < kBlocks; ++q) {
-        float zv[kVec];
-        widen_raw16<Elem>(zraw[q], zv);
+        for (int q = 0; q < kQuads; ++q)
+          lds_y[slot][q][lane] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+      }
+      __syncthreads();
+      if (half == 0) {
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) y[q * kVec + e] = gate_f(y[q * kVec + e], zv[e]);
+        for (int q = 0; q < kQuads; ++q) {
+          const float4 o = lds_y[slot][q][lane];
+          y[4 * q] += o.x;
+          y[4 * q + 1] += o.y;
+          y[4 * q + 2] += o.z;
+          y[4 * q + 3] += o.w;
+        }
       }
     }
-    store_lane_block<Elem, kVecRows, T>(out_buf, uint32_t(tb), y);
-    if (kCkpt && active && lane < N && 2 * c + 1 < p.n_ckpt)
+    if (half == 0) {  // the gate and the store: once per channel
+      if (p.z) {
+#pragma unroll
+        for (int q = 0; q < kBlocks; ++q) {
+          float zv[kVec];
+          widen_raw16<Elem>(zraw[q], zv);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) y[q * kVec + e] = gate_f(y[q * kVec + e], zv[e]);
+        }
+      }
+      store_lane_block<Elem, kVecRows, T>(out_buf, uint32_t(tb), y);
+    }
+    if (kCkpt && active && lane < N && own && 2 * c + 1 < p.n_ckpt)
       p.ckpt[(row * p.n_ckpt + 2 * c + 1) * N + lane] = mid_lane;
   }
 
-  if (active && p.final_state && lane < N) p.final_state[row * N + lane] = hc_lane;
+  if (active && p.final_state && lane < N && own) p.final_state[row * N + lane] = hc_lane;
 }
 
 __global__ void fill_zero_kernel(float* p, int64_t count) {
@@ -408,14 +445,34 @@ __global__ __launch_bounds__(64) void debug_wave_combine_kernel(const float* a, 
   b_out[i] = bv;
 }
 
+// Channels up to which an fp32 launch splits each channel's states over two waves. One wave
+// per channel leaves most SIMDs (256 CUs x 4) with a single wave; two per channel still all
+// fit at once up to 1024 channels (two waves per SIMD at this kernel's register count).
+// Past that the second wave of each channel would run in a second, partly empty round.
+constexpr int64_t kSplitMaxRows = 1024;
+
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kMask>
-void launch_flavour(bool ckpt, dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-  if (ckpt)
+void launch_flavour(bool ckpt, bool split, dim3 grid, dim3 block, hipStream_t s,
+                    const KParams& p) {
+  // The training forward takes the same form as the plain one, so that both write the same
+  // output bit for bit.
+  if (sizeof(Elem) == 4 && split) {
+    if constexpr (sizeof(Elem) == 4) {
+      const dim3 block2(block.x * 2);
+      if (ckpt)
+        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask, 2>), grid,
+                           block2, 0, s, p);
+      else
+        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask, 2>), grid,
+                           block2, 0, s, p);
+    }
+  } else if (ckpt) {
     hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask>), grid, block,
                        0, s, p);
-  else
+  } else {
     hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask>), grid,
                        block, 0, s, p);
+  }
 }
 
 template <typename Elem, int T, int K, int G, bool kDma>
@@ -442,16 +499,18 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
   p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
   const int64_t blocks = a.batch * p.dblocks;
   const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * K);
+  const bool ck = a.ckpt != nullptr;
+  const bool split = a.batch * a.dim <= kSplitMaxRows;
   if (a.vec_ok) {
     if (a.mask)
-      launch_flavour<Elem, T, K, G, true, kDma, true>(a.ckpt != nullptr, grid, block, s, p);
+      launch_flavour<Elem, T, K, G, true, kDma, true>(ck, split, grid, block, s, p);
     else
-      launch_flavour<Elem, T, K, G, true, kDma, false>(a.ckpt != nullptr, grid, block, s, p);
+      launch_flavour<Elem, T, K, G, true, kDma, false>(ck, split, grid, block, s, p);
   } else {
     if (a.mask)
-      launch_flavour<Elem, T, K, G, false, false, true>(a.ckpt != nullptr, grid, block, s, p);
+      launch_flavour<Elem, T, K, G, false, false, true>(ck, split, grid, block, s, p);
     else
-      launch_flavour<Elem, T, K, G, false, false, false>(a.ckpt != nullptr, grid, block, s, p);
+      launch_flavour<Elem, T, K, G, false, false, false>(ck, split, grid, block, s, p);
   }
   return int(hipGetLastError());
 }

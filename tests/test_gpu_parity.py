@@ -123,3 +123,18 @@ def test_parity_full_size_sampled(name):
     assert_parity(w.io, out[bi, di], fin[bi, di], ref_out, ref_fin,
                   f"{w.describe()} ({len(rows)} sampled rows)")
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(fin))
+
+
+@pytest.mark.parametrize("rows", [(1, 1023), (2, 512), (1, 1025), (3, 700)],
+                         ids=lambda r: "b{}d{}".format(*r))
+def test_parity_fp32_around_the_state_split(rows):
+    """fp32 launches with up to 1024 channels split each channel's states over two waves;
+    past that they use one wave per channel. Both sides of the threshold, every element."""
+    b, d = rows
+    w = SMALL.with_(batch=b, dim=d, dstate=16, seqlen=600, io="f32", gate=True,
+                    initial_state=True, seed=140 + d)
+    announce(w.describe())
+    inp = make_inputs(w)
+    got = run_hip(inp)
+    ref = oracle_full(inp)
+    assert_parity("f32", got[0], got[1], ref[0], ref[1], w.describe())
