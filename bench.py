@@ -52,7 +52,7 @@ FLOP_EQ_PER_UPDATE_NO_PACKED = 12
 # e = a g (1): 18 issue slots = 36 flop-equivalents.
 BWD_FLOP_EQ_PER_UPDATE = 36
 INFINITY_CACHE_BYTES = 256 << 20
-_CSRC = "selective_scan_fwd_amd/csrc/"
+_CSRC = "selective_state_space_fwd_amd/csrc/"
 _SHARED = [_CSRC + "device_math.h", _CSRC + "device_scan.h", _CSRC + "scan_launch.h"]
 KERNEL_SOURCES = {"fwd": [_CSRC + "scan_kernels.hip", _CSRC + "scan_short.hip"] + _SHARED,
                   "bwd": [_CSRC + "scan_bwd.hip"] + _SHARED,
@@ -221,7 +221,7 @@ def alu_probe(torch, steps: int, warmup: int) -> int:
     of wave64 v_exp_f32 (libssmprobe.so), at 16 waves per CU. Prints one JSON line."""
     import ctypes
 
-    from selective_scan_fwd_amd.build import PROBE_LIB_PATH
+    from selective_state_space_fwd_amd.build import PROBE_LIB_PATH
 
     if not os.path.exists(PROBE_LIB_PATH):
         raise RuntimeError(f"{PROBE_LIB_PATH} is missing: build first")
@@ -649,7 +649,7 @@ def main() -> int:
     if args.alu_probe:
         return alu_probe(torch, min(args.steps, 20), min(args.warmup, 3))
 
-    import selective_scan_fwd_amd as ssm
+    import selective_state_space_fwd_amd as ssm
     from ssm_workloads import SSD_WORKLOADS, WORKLOADS, make_inputs
 
     if args.workload in SSD_WORKLOADS:

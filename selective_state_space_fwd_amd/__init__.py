@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it first "
-                           "(python -m selective_scan_fwd_amd.build)")
+                           "(python -m selective_state_space_fwd_amd.build)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.ssm_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp,

@@ -1,6 +1,6 @@
 """Build libssmscan.so in-tree with hipcc for gfx950.
 
-    python -m selective_scan_fwd_amd.build
+    python -m selective_state_space_fwd_amd.build
 
 Every HIP source is compiled with the packed-fp32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns that it does

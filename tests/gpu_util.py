@@ -4,7 +4,7 @@ import sys
 
 import numpy as np
 
-import selective_scan_fwd_amd as ssm
+import selective_state_space_fwd_amd as ssm
 from ssm_workloads import bf16_bits_to_f32
 
 

@@ -9,8 +9,8 @@ import re
 
 import pytest
 
-import selective_scan_fwd_amd as ssm
-from selective_scan_fwd_amd.build import INCLUDE
+import selective_state_space_fwd_amd as ssm
+from selective_state_space_fwd_amd.build import INCLUDE
 
 HEADER = os.path.join(INCLUDE, "ssm_scan.h")
 HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
@@ -40,7 +40,7 @@ def test_exports_nothing_else():
     nm = shutil.which("nm")
     if nm is None:
         pytest.skip("nm not available")
-    from selective_scan_fwd_amd.build import LIB_PATH
+    from selective_state_space_fwd_amd.build import LIB_PATH
     out = subprocess.run([nm, "-D", "--defined-only", LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     text_syms = sorted(line.split()[-1] for line in out.splitlines()
@@ -241,7 +241,7 @@ def test_probe_library_exports_and_validates():
     library, exports its two calls, and refuses bad arguments before any HIP call."""
     import ctypes
 
-    from selective_scan_fwd_amd.build import PROBE_LIB_PATH
+    from selective_state_space_fwd_amd.build import PROBE_LIB_PATH
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     lib.ssm_probe_alu.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_void_p]

@@ -5,7 +5,7 @@ The backward entry point itself is checked against the float64 oracle in test_gp
 import numpy as np
 import pytest
 
-import selective_scan_fwd_amd as ssm
+import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, torch
 from ssm_workloads import WORKLOADS, make_inputs, make_mask
 

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-import selective_scan_fwd_amd as ssm
+import selective_state_space_fwd_amd as ssm
 from golden_io import load
 from gpu_util import announce, host, run_hip, torch
 from ssm_workloads import (RTOL, RTOL_STATE, WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits,

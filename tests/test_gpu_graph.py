@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-import selective_scan_fwd_amd as ssm
+import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, host, torch
 from ssm_workloads import (RTOL, RTOL_STATE, SSD_WORKLOADS, WORKLOADS, make_inputs,
                            make_ssd_inputs, parity, widen)

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-import selective_scan_fwd_amd as ssm
+import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, host, torch
 from ssm_workloads import (RTOL, RTOL_STATE, WORKLOADS, f32_to_bf16_bits, make_inputs,
                            make_mask, parity, widen)

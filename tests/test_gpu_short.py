@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-import selective_scan_fwd_amd as ssm
+import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, host, run_hip, torch
 from ssm_workloads import RTOL, RTOL_STATE, WORKLOADS, make_inputs, parity, widen
 
