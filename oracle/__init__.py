@@ -172,11 +172,13 @@ def _widen(x, io):
 
 
 def scan_rows(inputs: Dict[str, Optional[np.ndarray]], rows: Iterable[Tuple[int, int]],
-              delta_softplus: bool = True, nthreads: Optional[int] = None
-              ) -> Tuple[np.ndarray, np.ndarray]:
+              delta_softplus: bool = True, nthreads: Optional[int] = None,
+              precision: str = "f64") -> Tuple[np.ndarray, np.ndarray]:
     """Oracle outputs for selected (b, d) rows of a workload given in storage form
     (float32 arrays, or bf16 bit patterns when inputs['io'] == 'bf16').
-    Returns out_rows [R, L] and final_rows [R, N] in float64."""
+    Returns out_rows [R, L] and final_rows [R, N] in float64. Each row is computed by
+    ``scan_ref`` on that row's slices alone (u, delta, z [b, d]; B, C [b]; A, D, bias [d];
+    h0 [b, d]), so it equals the same row of a whole-tensor ``scan_ref`` call bit for bit."""
     io = inputs["io"]
     rows = list(rows)
     L = inputs["u"].shape[2]
@@ -196,7 +198,7 @@ def scan_rows(inputs: Dict[str, Optional[np.ndarray]], rows: Iterable[Tuple[int,
             delta_softplus,
             None if inputs.get("h0") is None else np.asarray(inputs["h0"][b:b + 1, d:d + 1],
                                                               np.float64),
-            nthreads=1,
+            nthreads=1, precision=precision,
         )
         outs[i] = o[0, 0]
         fins[i] = f[0, 0]

@@ -443,3 +443,82 @@ def test_interior_padding_is_deleting_those_steps():
     comp = {k: (v[..., keep] if k in ("u", "delta", "z", "B", "C") else v) for k, v in inp.items()}
     o, f = _run(comp)
     assert np.array_equal(out[0][:, keep], o[0]) and np.array_equal(fin, f)
+
+
+# ---------------------------------------------------------------- row sampling (scan_rows)
+
+def _whole(inp, precision):
+    from ssm_workloads import widen
+    io = inp["io"]
+    return oracle.scan_ref(widen(inp["u"], io), widen(inp["delta"], io), inp["A"],
+                           widen(inp["B"], io), widen(inp["C"], io), inp["D"],
+                           widen(inp["z"], io), inp["delta_bias"], True, inp["h0"],
+                           nthreads=2, precision=precision)
+
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+@pytest.mark.parametrize("kind", ["f32", "bf16-gated-h0"])
+def test_scan_rows_equals_the_whole_scan(kind, precision):
+    """The sampled-row oracle behind the full-size parity checks: over every (b, d) of a
+    small workload it must return exactly the rows of one whole-tensor scan. A slip in its
+    slicing (B or C of the wrong batch row, A or D of the wrong channel, the wrong h0 row,
+    a missing bias or gate, bf16 not widened) changes a row and fails here."""
+    from ssm_workloads import Workload, make_inputs
+    if kind == "f32":
+        w = Workload("rows", 2, 5, 3, 70, "f32", seed=11)
+    else:
+        w = Workload("rows", 3, 4, 17, 90, "bf16", gate=True, a_kind="scaled",
+                     bc_scale=0.125, initial_state=True, seed=12)
+    inp = make_inputs(w)
+    out, fin = _whole(inp, precision)
+    rows = [(b, d) for b in range(w.batch) for d in range(w.dim)]
+    ro, rf = oracle.scan_rows(inp, rows, delta_softplus=True, precision=precision)
+    assert np.array_equal(ro, out.reshape(w.batch * w.dim, w.seqlen).astype(np.float64))
+    assert np.array_equal(rf, fin.reshape(w.batch * w.dim, w.dstate).astype(np.float64))
+    # rows in a scrambled order come back in that order
+    pick = [rows[i] for i in (7, 0, len(rows) - 1, 3)]
+    so, sf = oracle.scan_rows(inp, pick, delta_softplus=True, precision=precision)
+    for i, (b, d) in enumerate(pick):
+        assert np.array_equal(so[i], out[b, d].astype(np.float64))
+        assert np.array_equal(sf[i], fin[b, d].astype(np.float64))
+
+
+def test_sample_rows_covers_the_ends():
+    rows = oracle.sample_rows(4, 2048, 64, seed=2)
+    assert rows[0] == (0, 0) and rows[-1] == (3, 2047)
+    assert len(set(rows)) == len(rows) and rows == sorted(rows)
+    assert all(0 <= b < 4 and 0 <= d < 2048 for b, d in rows)
+
+
+# ---------------------------------------------------------------- the float32 instantiation
+
+def test_f32_instantiation_brute_force_and_decay():
+    """ssm_ref_scan_f32 (used only to report the float32 rounding floor) against the
+    brute-force expansion and the decay example, where A != 0, so its exp, log1p and
+    softplus branch are exercised; float32 rounding bounds the distance."""
+    rng = np.random.default_rng(13)
+    batch, dim, N, L = 2, 3, 5, 7
+    u = rng.standard_normal((batch, dim, L))
+    delta = 0.5 * rng.standard_normal((batch, dim, L))
+    bias = np.log(np.expm1(rng.uniform(1e-3, 1e-1, dim)))
+    A = -rng.uniform(0.5, 8.0, (dim, N))
+    Bm = rng.standard_normal((batch, N, L))
+    Cm = rng.standard_normal((batch, N, L))
+    Dv = rng.standard_normal(dim)
+    z = rng.standard_normal((batch, dim, L))
+    h0 = rng.standard_normal((batch, dim, N))
+    f32 = lambda x: np.asarray(x, np.float32).astype(np.float64)  # the values f32 sees
+    args = [f32(x) for x in (u, delta, A, Bm, Cm, Dv, z, bias)]
+    out, fin = run(*args, True, f32(h0), precision="f32")
+    ob, fb = brute_force(*args[:6], args[6], args[7], f32(h0))
+    for g, r in ((out, ob), (fin, fb)):
+        scale = np.abs(r) + np.sqrt(np.mean(r ** 2))
+        assert np.max(np.abs(g - r) / scale) < 2e-6
+    g = load("decay.txt")
+    steps = int(g["steps"][0])
+    for a, approx, tol in zip(g["a"], g["approx"], g["printed_abs_tolerance"]):
+        _, fin = run(np.zeros((1, 1, steps)), np.ones((1, 1, steps)), np.array([[math.log(a)]]),
+                     np.zeros((1, 1, steps)), np.zeros((1, 1, steps)), h0=np.ones((1, 1, 1)),
+                     precision="f32")
+        assert abs(float(fin[0, 0, 0]) - approx) <= tol
+        assert float(fin[0, 0, 0]) == pytest.approx(a ** steps, rel=1e-4)
