@@ -39,6 +39,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
 # slot as one FMA (2 flop), an update is 16 flop-equivalents against the 157.3 peak.
 ALU_PEAK_TFLOPS = 157.3
 FLOP_EQ_PER_UPDATE = 16
+# The method's own arithmetic per update, as the roofline counts it: dt*A and (dt*u)*B (two
+# mul), h = dA*h + dBu and y += C*h (two FMA, 4 flop): 6 flop, plus one exp. A transcendental
+# retires at a quarter of the FMA rate, so the exp peak is 157.3e12 / 2 / 4 per second.
+FLOPS_PER_UPDATE = 6
+EXPS_PER_UPDATE = 1
+EXP_PEAK_PER_S = ALU_PEAK_TFLOPS * 1e12 / 2 / 4
 # The 157.3 TFLOP/s figure needs packed fp32 (v_pk_fma_f32: two fp32 FMAs per lane per
 # instruction), which this build disables. Without it a SIMD retires 16 fp32 FMA lanes per
 # clock: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz = 78.6 TFLOP/s, a wave64 v_fma_f32
@@ -239,7 +245,11 @@ def alu_probe(torch, steps: int, warmup: int) -> int:
     res = {"probe": "alu", "cus": cus, "waves_per_cu": 16,
            "note": "packed fp32 disabled at build time; lane-ops per second, and clocks per "
                    "wave64 instruction per SIMD at the 2.4 GHz peak clock"}
-    for kind, name in ((0, "v_fma_f32"), (1, "v_exp_f32")):
+    lib.ssm_probe_fma_per_exp.argtypes = [ctypes.c_int]
+    lib.ssm_probe_fma_per_exp.restype = ctypes.c_int
+    secs = {}
+    for kind, name in ((0, "v_fma_f32"), (1, "v_exp_f32"), (2, "mix_4fma_1exp"),
+                       (3, "mix_2fma_1exp"), (4, "mix_1fma_1exp")):
         launch = lambda: lib.ssm_probe_alu(kind, blocks, iters, out.data_ptr(),
                                            stream.cuda_stream)
         for _ in range(warmup):
@@ -253,14 +263,76 @@ def alu_probe(torch, steps: int, warmup: int) -> int:
         b.record(stream)
         torch.cuda.synchronize()
         sec = a.elapsed_time(b) * 1e-3 / steps
+        secs[kind] = sec
         ops = lib.ssm_probe_ops_per_launch(blocks, iters)
         wave_instr_per_simd = ops / 64 / (cus * 4)
-        res[name] = {"lane_ops_per_s": round(ops / sec, 1),
-                     "clk_per_wave_instr_at_2p4GHz": round(sec * 2.4e9 / wave_instr_per_simd, 3)}
+        if kind < 2:
+            res[name] = {"lane_ops_per_s": round(ops / sec, 1),
+                         "clk_per_wave_instr_at_2p4GHz": round(sec * 2.4e9 / wave_instr_per_simd,
+                                                               3)}
+        else:
+            # ops FMA lane-operations plus ops / r exps: compare with the two streams run
+            # one after the other (no overlap) and with the longer of the two alone.
+            r = lib.ssm_probe_fma_per_exp(kind)
+            serial = secs[0] + secs[1] / r
+            res[name] = {"us_per_launch": round(sec * 1e6, 2),
+                         "serial_model_us": round(serial * 1e6, 2),
+                         "overlap_model_us": round(max(secs[0], secs[1] / r) * 1e6, 2),
+                         "measured_over_serial": round(sec / serial, 4)}
     fma = res["v_fma_f32"]["lane_ops_per_s"]
     res["v_fma_f32"]["TFLOPs"] = round(2 * fma / 1e12, 2)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def forward_roofline(w, set_bytes: int, avg_ms: float, traffic, kernel: str) -> dict:
+    """The forward's roofline on the metric's own basis: algorithmic bytes per launch over
+    the mean launch time (HIP events on the launch stream), against the 8 TB/s HBM peak.
+
+    Beside it, two compute views, labelled as such:
+      * "alu": the method's arithmetic as counted per (b, d, n, t) update (dt*A, (dt*u)*B,
+        the state FMA and the output FMA: 6 flop, plus one exp), against the 157.3 TFLOP/s
+        fp32 vector peak and the exp rate that peak implies (a transcendental at a quarter
+        of the FMA rate: 157.3e12 / 2 / 4 per second). On this count the HBM floor is the
+        longer one, so the binding roof is HBM.
+      * "alu_issue_no_packed": what the kernel can actually issue with packed fp32 disabled
+        (4 wave64 VALU instructions at 4 clocks and one v_exp_f32 at 8 per update: 12
+        flop-equivalents against 78.6 TFLOP/s), the floor the kernel is really measured
+        against.
+    """
+    t = avg_ms * 1e-3
+    achieved = set_bytes / t / 1e9
+    t_hbm = set_bytes / (HBM_PEAK_GBS * 1e9)
+    flops = FLOPS_PER_UPDATE * w.tuples
+    exps = EXPS_PER_UPDATE * w.tuples
+    t_flop = flops / (ALU_PEAK_TFLOPS * 1e12)
+    t_exp = exps / EXP_PEAK_PER_S
+    np_work = FLOP_EQ_PER_UPDATE_NO_PACKED * w.tuples
+    np_achieved = np_work / t / 1e12
+    return {
+        "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+        "kernel_hash": kernel_hash(),
+        "work": (f"{set_bytes} algorithmic bytes per launch (each input read once, each output "
+                 f"written once) over the mean launch time {avg_ms * 1e3:.3f} us"),
+        "floor_us": {"hbm": round(t_hbm * 1e6, 3), "alu_flops": round(t_flop * 1e6, 3),
+                     "alu_exp": round(t_exp * 1e6, 3),
+                     "alu_issue_no_packed": round(np_work / (ALU_PEAK_NO_PACKED_TFLOPS * 1e12)
+                                                  * 1e6, 3)},
+        "alu": {"flops_per_update": FLOPS_PER_UPDATE, "exps_per_update": EXPS_PER_UPDATE,
+                "achieved": round(flops / t / 1e12, 3), "peak": ALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / ALU_PEAK_TFLOPS, 4),
+                "exp_achieved_per_s": round(exps / t, 1), "exp_peak_per_s": EXP_PEAK_PER_S,
+                "exp_frac": round(exps / t / EXP_PEAK_PER_S, 4)},
+        "alu_issue_no_packed": {
+            "achieved": round(np_achieved, 3), "peak": ALU_PEAK_NO_PACKED_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(np_achieved / ALU_PEAK_NO_PACKED_TFLOPS, 4),
+            "work": (f"{FLOP_EQ_PER_UPDATE_NO_PACKED} flop-equivalents per update (4 wave64 "
+                     "VALU instructions at 4 clocks + 1 v_exp_f32 at 8 clocks) x "
+                     f"{w.tuples} updates per launch"),
+            "basis": "the build disables packed fp32 (v_pk_fma_f32), which the 157.3 TFLOP/s "
+                     "peak needs; this is the peak of the instructions the kernel can issue"},
+    }
 
 
 def timed_launches(launch, steps, warmup, stream, torch):
@@ -736,37 +808,10 @@ def main() -> int:
 
     value = set_bytes * K / wall / 1e9
     avg_ms = float(kern_ms.mean())
-    achieved = set_bytes / (avg_ms * 1e-3) / 1e9
-    alu_achieved = FLOP_EQ_PER_UPDATE * w.tuples / (avg_ms * 1e-3) / 1e12
+    med_ms = float(np.median(kern_ms))
     traffic = load_traffic(args.workload)
     kernel = "scan_short_kernel" if w.seqlen <= SHORT_MAX_SEQLEN else "scan_fwd_kernel"
-    alu = {"achieved": round(alu_achieved, 3), "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-           "frac": round(alu_achieved / ALU_PEAK_TFLOPS, 4),
-           "work": (f"{FLOP_EQ_PER_UPDATE} flop-equivalents per (b,d,n,t) update (2 mul + 2 fma "
-                    "+ 1 exp at quarter rate = 8 FMA issue slots) x "
-                    f"{w.tuples} updates per launch")}
-    hbm = {"achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": round(achieved / HBM_PEAK_GBS, 4),
-           "work": f"{set_bytes} algorithmic bytes per launch"}
-    # The binding roof is the one whose floor time is longer for this workload.
-    t_alu = FLOP_EQ_PER_UPDATE * w.tuples / (ALU_PEAK_TFLOPS * 1e12)
-    t_hbm = set_bytes / (HBM_PEAK_GBS * 1e9)
-    main, other = (("alu", alu), ("hbm", hbm)) if t_alu >= t_hbm else (("hbm", hbm), ("alu", alu))
-    roofline = {"bound": main[0], **main[1], "traffic": traffic, "kernel": kernel,
-                "kernel_hash": kernel_hash(),
-                "floor_us": {"alu": round(t_alu * 1e6, 3), "hbm": round(t_hbm * 1e6, 3)},
-                other[0]: other[1]}
-    np_work = FLOP_EQ_PER_UPDATE_NO_PACKED * w.tuples
-    np_achieved = np_work / (avg_ms * 1e-3) / 1e12
-    roofline["alu_no_packed_fp32"] = {
-        "achieved": round(np_achieved, 3), "peak": ALU_PEAK_NO_PACKED_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(np_achieved / ALU_PEAK_NO_PACKED_TFLOPS, 4),
-        "floor_us": round(np_work / (ALU_PEAK_NO_PACKED_TFLOPS * 1e12) * 1e6, 3),
-        "work": (f"{FLOP_EQ_PER_UPDATE_NO_PACKED} flop-equivalents per update (4 wave64 VALU "
-                 "instructions at 4 clocks + 1 v_exp_f32 at 8 clocks) x "
-                 f"{w.tuples} updates per launch"),
-        "basis": "the build disables packed fp32 (v_pk_fma_f32), which the 157.3 TFLOP/s "
-                 "peak needs; this is the peak of the instructions the kernel can issue"}
+    roofline = forward_roofline(w, set_bytes, avg_ms, traffic, kernel)
 
     result = {
         "metric": ("scan GB/s & % HBM peak (1 MI355X), b4 d2048 N16 L2048 bf16"
@@ -794,9 +839,13 @@ def main() -> int:
         "elements_per_s": round(w.elements * K / wall, 1),
         "tuples_per_s": round(w.tuples * K / wall, 1),
         "kernel_us": {"mean": round(avg_ms * 1e3, 3),
-                      "median": round(float(np.median(kern_ms)) * 1e3, 3),
+                      "median": round(med_ms * 1e3, 3),
                       "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
                       "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
+        "per_launch_GBps": {"mean": round(set_bytes / (avg_ms * 1e-3) / 1e9, 2),
+                            "median": round(set_bytes / (med_ms * 1e-3) / 1e9, 2),
+                            "note": "algorithmic bytes over one launch's event time; value is "
+                                    "the whole job's wall clock, gaps between launches included"},
         "roofline": roofline,
         "warm": warm,
     }

@@ -69,6 +69,15 @@ extern "C" {
 #define SSM_DELTA_SOFTPLUS (1u << 4)
 /* final_state is in/out: read as h_{-1}, overwritten with h_{L-1} */
 #define SSM_INITIAL_STATE (1u << 5)
+/* Launch-shape hints for the chunked scan (seqlen > 32), forward entry points only: how many
+ * wavefronts share one channel's states. With neither bit the library chooses: fp32 launches
+ * whose workgroups all fit on the device at once take two waves per channel, every other
+ * launch one. Two waves per channel exist for fp32 storage only (SSM_ERR_UNSUPPORTED with
+ * bf16); setting both bits is SSM_ERR_INVALID_ARG. The two forms compute every state in the
+ * same order (final and saved states bitwise equal) and sum y over the states in a different
+ * order (outputs equal to fp32 rounding). Sequences of at most 32 steps ignore the hint. */
+#define SSM_WAVES_PER_CHANNEL_1 (1u << 8)
+#define SSM_WAVES_PER_CHANNEL_2 (1u << 9)
 
 /* status codes */
 #define SSM_OK 0

@@ -31,6 +31,8 @@ SSM_IO_F32 = 0
 SSM_IO_BF16 = 1
 SSM_DELTA_SOFTPLUS = 1 << 4
 SSM_INITIAL_STATE = 1 << 5
+SSM_WAVES_PER_CHANNEL_1 = 1 << 8
+SSM_WAVES_PER_CHANNEL_2 = 1 << 9
 
 SSM_OK = 0
 SSM_ERR_INVALID_ARG = -1
@@ -220,8 +222,18 @@ def _check_mask(mask, u, batch, seqlen):
     return mask
 
 
+def _hint_flags(waves_per_channel) -> int:
+    if waves_per_channel is None:
+        return 0
+    if waves_per_channel == 1:
+        return SSM_WAVES_PER_CHANNEL_1
+    if waves_per_channel == 2:
+        return SSM_WAVES_PER_CHANNEL_2
+    raise ValueError("waves_per_channel must be None, 1 or 2")
+
+
 def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final_state,
-             return_final_state, save_states, mask=None):
+             return_final_state, save_states, mask=None, waves_per_channel=None):
     import torch
 
     u, delta, A, B, C, D, z, delta_bias, h0, mask = _dense(u, delta, A, B, C, D, z, delta_bias,
@@ -249,6 +261,7 @@ def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final
         final_state = torch.empty((batch, dim, dstate), device=u.device, dtype=torch.float32)
     if delta_softplus:
         flags |= SSM_DELTA_SOFTPLUS
+    flags |= _hint_flags(waves_per_channel)
     args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             flags, _ptr(out), _ptr(final_state))
     sizes = (batch, dim, dstate, seqlen, _stream_of(u.device))
@@ -268,26 +281,27 @@ def _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out, final
 
 
 def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
-         h0=None, out=None, final_state=None, return_final_state: bool = True, mask=None
-         ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+         h0=None, out=None, final_state=None, return_final_state: bool = True, mask=None,
+         waves_per_channel=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Selective-scan forward on the GPU.
 
     u, delta, z: [batch, dim, seqlen]; B, C: [batch, dstate, seqlen] (float32 or bfloat16,
     all the same dtype); A: [dim, dstate], D and delta_bias: [dim], h0: [batch, dim,
     dstate] (float32); mask: [batch, seqlen] uint8/bool, 0 = padding step (the state is
-    kept). Returns (out, final_state); out has u's dtype.
+    kept). waves_per_channel: None (the library chooses), 1 or 2 (fp32 only): the
+    SSM_WAVES_PER_CHANNEL_* launch-shape hint. Returns (out, final_state); out has u's dtype.
     """
     out, fin, _ = _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, out,
-                           final_state, return_final_state, False, mask)
+                           final_state, return_final_state, False, mask, waves_per_channel)
     return out, fin
 
 
 def scan_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
-               h0=None, mask=None):
+               h0=None, mask=None, waves_per_channel=None):
     """``scan`` that also returns the states the backward pass restarts from:
     (out, final_state, chunk_states [batch, dim, ceil(seqlen / 512), dstate] float32)."""
     return _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, None, None, True,
-                    True, mask)
+                    True, mask, waves_per_channel)
 
 
 def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_bias=None,

@@ -22,7 +22,7 @@ using ssm_api::span;
 
 extern "C" {
 
-int ssm_scan_abi_version(void) { return 3; }
+int ssm_scan_abi_version(void) { return 4; }
 
 const char* ssm_scan_strerror(int status) {
   switch (status) {
@@ -55,14 +55,17 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
              const float* D, const void* z, const float* delta_bias, const uint8_t* mask,
              uint32_t flags, void* out, float* final_state, float* ckpt, bool want_ckpt,
              int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, void* stream) {
-  const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
+  const uint32_t hints = SSM_WAVES_PER_CHANNEL_1 | SSM_WAVES_PER_CHANNEL_2;
+  const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE | hints;
   if (flags & ~known) return SSM_ERR_INVALID_ARG;
+  if ((flags & hints) == hints) return SSM_ERR_INVALID_ARG;
   if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return SSM_ERR_INVALID_ARG;
   const bool initial_state = (flags & SSM_INITIAL_STATE) != 0;
 
   const uint32_t io = flags & SSM_IO_MASK;
   if (io != SSM_IO_F32 && io != SSM_IO_BF16) return SSM_ERR_UNSUPPORTED;
   if (dstate < 1 || dstate > 64) return SSM_ERR_UNSUPPORTED;
+  if (io == SSM_IO_BF16 && (flags & SSM_WAVES_PER_CHANNEL_2)) return SSM_ERR_UNSUPPORTED;
   const int64_t esz = (io == SSM_IO_BF16) ? 2 : 4;
 
   int64_t rows, elems, elems_bytes, bc, bc_bytes, state, state_bytes, a_elems;
@@ -142,6 +145,8 @@ int fwd_impl(const void* u, const void* delta, const float* A, const void* B, co
              aligned(B, 16) && aligned(C, 16) && aligned(out, 16) && (!z || aligned(z, 16));
   a.ckpt = want_ckpt ? ckpt : nullptr;
   a.mask = mask;
+  a.waves_per_channel = (flags & SSM_WAVES_PER_CHANNEL_1) ? 1
+                        : (flags & SSM_WAVES_PER_CHANNEL_2) ? 2 : 0;
   return ssm::launch_scan_fwd(a, stream) == 0 ? SSM_OK : SSM_ERR_HIP;
 }
 

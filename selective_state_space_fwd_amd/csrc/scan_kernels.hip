@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "device_math.h"
 #include "device_scan.h"
 #include "scan_launch.h"
@@ -445,11 +447,32 @@ __global__ __launch_bounds__(64) void debug_wave_combine_kernel(const float* a, 
   b_out[i] = bv;
 }
 
-// Channels up to which an fp32 launch splits each channel's states over two waves. One wave
-// per channel leaves most SIMDs (256 CUs x 4) with a single wave; two per channel still all
-// fit at once up to 1024 channels (two waves per SIMD at this kernel's register count).
-// Past that the second wave of each channel would run in a second, partly empty round.
-constexpr int64_t kSplitMaxRows = 1024;
+// Compute units of the current device, read once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Whether an fp32 launch splits each channel's states over two waves. One wave per channel
+// leaves most SIMDs with a single wave when there are few channels. A two-wave workgroup (K
+// channels, 2K waves at about 192 VGPRs, two waves per SIMD) fills a compute unit, so the
+// split pays only while every workgroup runs at once: past one workgroup per compute unit the
+// second wave of each channel would wait for a second, partly empty round.
+bool fp32_split(int64_t workgroups, int waves_per_channel) {
+  if (waves_per_channel != 0) return waves_per_channel == 2;
+  const int cus = device_cus();
+  return cus > 0 && workgroups <= cus;
+}
 
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kMask>
 void launch_flavour(bool ckpt, bool split, dim3 grid, dim3 block, hipStream_t s,
@@ -500,7 +523,7 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
   const int64_t blocks = a.batch * p.dblocks;
   const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * K);
   const bool ck = a.ckpt != nullptr;
-  const bool split = a.batch * a.dim <= kSplitMaxRows;
+  const bool split = sizeof(Elem) == 4 && fp32_split(blocks, a.waves_per_channel);
   if (a.vec_ok) {
     if (a.mask)
       launch_flavour<Elem, T, K, G, true, kDma, true>(ck, split, grid, block, s, p);

@@ -26,6 +26,7 @@ struct FwdArgs {
   bool vec_ok;             // every row of every streamed array starts 16-byte aligned
   float* ckpt = nullptr;   // nullable: states every kCkptInterval steps [rows, n_ckpt, dstate]
   const uint8_t* mask = nullptr;  // nullable: [batch, seqlen], 0 = padding step
+  int waves_per_channel = 0;      // chunked fp32 scan: 1 or 2, 0 = chosen from the launch size
 };
 
 // Spacing of the saved states that the backward pass restarts from (the state entering

@@ -37,8 +37,10 @@ def host(x):
     return x.detach().cpu().numpy().astype(np.float64)
 
 
-def run_hip(inputs, softplus=True, use_D=True, use_z=True, use_bias=True, device="cuda"):
-    """Run the GPU scan on a workload dict (storage form). Returns (out, final) float64."""
+def run_hip(inputs, softplus=True, use_D=True, use_z=True, use_bias=True, device="cuda",
+            waves_per_channel=None):
+    """Run the GPU scan on a workload dict (storage form). Returns (out, final) float64.
+    waves_per_channel: the launch-shape hint (None: the library chooses)."""
     io = inputs["io"]
     g = {k: dev(inputs[k], io, device) for k in ("u", "delta", "B", "C", "z")}
     f = {k: dev(inputs[k], "f32", device) for k in ("A", "D", "delta_bias", "h0")}
@@ -46,6 +48,7 @@ def run_hip(inputs, softplus=True, use_D=True, use_z=True, use_bias=True, device
                         D=f["D"] if use_D else None,
                         z=g["z"] if use_z else None,
                         delta_bias=f["delta_bias"] if use_bias else None,
-                        delta_softplus=softplus, h0=f["h0"])
+                        delta_softplus=softplus, h0=f["h0"],
+                        waves_per_channel=waves_per_channel)
     torch().cuda.synchronize()
     return host(out), host(fin)

@@ -60,7 +60,7 @@ def test_header_constants_match_binding():
 
 
 def test_abi_version_and_strerror():
-    assert ssm.ssm_scan_abi_version() == 3
+    assert ssm.ssm_scan_abi_version() == 4
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(ssm.ssm_scan_strerror(s), str) and ssm.ssm_scan_strerror(s)
 
@@ -81,6 +81,7 @@ def call(**kw):
     dict(batch=-1), dict(dim=-1), dict(seqlen=-1), dict(dstate=-1),
     dict(flags=1 << 7), dict(flags=1 << 2), dict(flags=1 << 31),
     dict(flags=ssm.SSM_INITIAL_STATE),                       # initial state without final_state
+    dict(flags=ssm.SSM_WAVES_PER_CHANNEL_1 | ssm.SSM_WAVES_PER_CHANNEL_2),  # both hints
     dict(out=U), dict(out=DL + 16), dict(out=B), dict(out=C - 8), dict(z=OUT + 4),
     dict(final_state=OUT), dict(out=A),
 ])
@@ -91,6 +92,7 @@ def test_invalid_arguments(kw):
 @pytest.mark.parametrize("kw", [
     dict(dstate=0), dict(dstate=65), dict(dstate=1000), dict(flags=2), dict(flags=3),
     dict(batch=1 << 40, dim=1 << 40), dict(seqlen=1 << 33), dict(batch=1 << 20, dim=1 << 12),
+    dict(flags=ssm.SSM_IO_BF16 | ssm.SSM_WAVES_PER_CHANNEL_2),  # two waves: fp32 only
 ])
 def test_unsupported(kw):
     assert call(**kw) == ssm.SSM_ERR_UNSUPPORTED
@@ -112,6 +114,17 @@ def test_empty_is_a_noop():
     # seqlen == 0 with an in/out state and no output state to clear: nothing to do
     assert call(seqlen=0, flags=ssm.SSM_INITIAL_STATE, final_state=FIN) == ssm.SSM_OK
     assert call(seqlen=0) == ssm.SSM_OK
+
+
+def test_launch_hints_pass_validation():
+    # each hint alone is a valid flag: the call gets past every check (here, with no device,
+    # it then fails at the launch or at the empty-shape early return)
+    for f in (ssm.SSM_WAVES_PER_CHANNEL_1, ssm.SSM_WAVES_PER_CHANNEL_2,
+              ssm.SSM_WAVES_PER_CHANNEL_1 | ssm.SSM_IO_BF16):
+        assert call(flags=f, batch=0) == ssm.SSM_OK
+        assert call(flags=f) in (ssm.SSM_OK, ssm.SSM_ERR_HIP)
+    with pytest.raises(ValueError):
+        ssm._hint_flags(3)
 
 
 def test_debug_wave_combine_validation():
@@ -248,6 +261,6 @@ def test_probe_library_exports_and_validates():
     lib.ssm_probe_ops_per_launch.argtypes = [ctypes.c_int64, ctypes.c_int]
     lib.ssm_probe_ops_per_launch.restype = ctypes.c_int64
     assert lib.ssm_probe_ops_per_launch(4, 200) == 4 * 256 * 200 * 32 * 8
-    assert lib.ssm_probe_alu(2, 4, 1, 16, None) == -1       # unknown kind
+    assert lib.ssm_probe_alu(5, 4, 1, 16, None) == -1       # unknown kind
     assert lib.ssm_probe_alu(0, 0, 1, 16, None) == -1       # no blocks
     assert lib.ssm_probe_alu(0, 4, 1, None, None) == -1     # no output

@@ -128,8 +128,9 @@ def test_parity_full_size_sampled(name):
 @pytest.mark.parametrize("rows", [(1, 1023), (2, 512), (1, 1025), (3, 700)],
                          ids=lambda r: "b{}d{}".format(*r))
 def test_parity_fp32_around_the_state_split(rows):
-    """fp32 launches with up to 1024 channels split each channel's states over two waves;
-    past that they use one wave per channel. Both sides of the threshold, every element."""
+    """fp32 launches whose workgroups (4 channels each) all fit on the device at once split
+    each channel's states over two waves; larger ones use one wave per channel. Both sides of
+    the threshold on a 256-CU device (256 and 257 workgroups), every element."""
     b, d = rows
     w = SMALL.with_(batch=b, dim=d, dstate=16, seqlen=600, io="f32", gate=True,
                     initial_state=True, seed=140 + d)
