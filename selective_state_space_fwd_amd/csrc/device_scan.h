@@ -13,6 +13,15 @@ __device__ __forceinline__ float readlane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// v_writelane_b32: the LLVM intrinsic, which this compiler exposes under no builtin name;
+// declared through its symbol so that the compiler sees it (and inserts its hazard waits).
+__device__ int ssm_llvm_writelane(int value, int lane, int old) __asm("llvm.amdgcn.writelane");
+
+// `old` with lane `lane` (uniform) replaced by the uniform value `v`.
+__device__ __forceinline__ float writelane(float old, float v, int lane) {
+  return __int_as_float(ssm_llvm_writelane(__float_as_int(v), lane, __float_as_int(old)));
+}
+
 // Elements per 16-byte access.
 template <typename Elem>
 struct Vec;

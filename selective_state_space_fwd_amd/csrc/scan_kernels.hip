@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
   const Buf B_buf(static_cast<const Elem*>(p.B) + int64_t(b) * N * L, bc_elems * kEsz);
   const Buf C_buf(static_cast<const Elem*>(p.C) + int64_t(b) * N * L, bc_elems * kEsz);
 
-  float Dd = 0.0f, bias_d = 0.0f, a2_lane = 0.0f, hc_lane = 0.0f, mid_lane = 0.0f;
+  float Dd = 0.0f, bias_d = 0.0f, a2_lane = 0.0f, hc_lane = 0.0f;
   if (active) {
     Dd = p.D ? p.D[d] : 0.0f;
     bias_d = p.bias ? p.bias[d] : 0.0f;
@@ -232,8 +232,15 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
   float dt[T], du[T], y[T];
   float sdt = 0.0f;
 
-  // One state group: the B/C words of stage `it` are in lds_bc[it & 1].
-  auto compute_group = [&](int it, int g) {
+  // Training forward: this row's saved states, [n_ckpt][N] fp32.
+  const Buf ck_buf(kCkpt ? p.ckpt + row * int64_t(p.n_ckpt) * N : nullptr,
+                   kCkpt && active ? uint32_t(p.n_ckpt) * uint32_t(N) * 4u : 0u);
+  // The saved state in the middle of a chunk is the state after step kCkptInterval - 1 of
+  // the chunk: the inclusive scan result of the lane whose segment ends there.
+  constexpr int kMidLane = kCkptInterval / T - 1;
+
+  // One state group: the B/C words of stage `it` (chunk c) are in lds_bc[it & 1].
+  auto compute_group = [&](int it, int c, int g) {
     const int buf = it & 1;
 #pragma unroll
     for (int nl = 0; nl < G; ++nl) {
@@ -267,22 +274,21 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
         for (int q = 0; q < kQuads; ++q) cq[q] = Cq[q * 64];
         float aseg = exp2_hw(sdt * a2);
         wave_scan_inclusive(aseg, bseg);  // bseg: state at the end of this lane's steps
-        const float carry_out = readlane(bseg, 63);
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
-        hc_lane = (lane == n) ? carry_out : hc_lane;
+        hc_lane = writelane(hc_lane, readlane(bseg, 63), n);  // carry into the next chunk
         if constexpr (kCkpt) {
-          // the state after the first half of the chunk: the last step of the lane before
-          // the one whose segment starts at kCkptInterval
-          const float mid = readlane(bseg, kCkptInterval / T - 1);
-          mid_lane = (lane == n) ? mid : mid_lane;
+          if (lane == kMidLane && 2 * c + 1 < p.n_ckpt)
+            ck_buf.store4(__float_as_uint(bseg), uint32_t((2 * c + 1) * N + n) * 4u);
         }
+        // Replay the lane's steps from the carried-in state. The state after the last step
+        // is the scan's inclusive result itself.
 #pragma unroll
         for (int q = 0; q < kQuads; ++q) {
           const float cc[4] = {cq[q].x, cq[q].y, cq[q].z, cq[q].w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = 4 * q + r;
-            h = __builtin_fmaf(dA[j], h, dBu[j]);
+            h = (j == T - 1) ? bseg : __builtin_fmaf(dA[j], h, dBu[j]);
             y[j] = __builtin_fmaf(cc[r], h, y[j]);
           }
         }
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
     const int tb = c * kChunk + lane * T;
     sdt = 0.0f;
     if (kCkpt && active && lane < N && own)  // the state entering the chunk
-      p.ckpt[(row * p.n_ckpt + 2 * c) * N + lane] = hc_lane;
+      ck_buf.store4(__float_as_uint(hc_lane), uint32_t(2 * c * N + lane) * 4u);
     {
       const bool tail = (c + 1) * kChunk > L;
 #pragma unroll
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
         asm volatile("" ::: "memory");  // the DMA stays ahead of the z loads below
       }
       if (g == n_groups - 1 && half == 0) load_z(c);
-      if (active) compute_group(it, g);
+      if (active) compute_group(it, c, g);
       stage_commit((it + 1) & 1);
       if constexpr (kDmaInputs) {
         // A bare s_barrier: with a release fence the compiler would wait for the DMA of the
@@ -422,8 +428,6 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
       }
       store_lane_block<Elem, kVecRows, T>(out_buf, uint32_t(tb), y);
     }
-    if (kCkpt && active && lane < N && own && 2 * c + 1 < p.n_ckpt)
-      p.ckpt[(row * p.n_ckpt + 2 * c + 1) * N + lane] = mid_lane;
   }
 
   if (active && p.final_state && lane < N && own) p.final_state[row * N + lane] = hc_lane;
