@@ -57,13 +57,20 @@ class SsmScanError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """Load libssmscan.so (built in-tree by build.py). Raises if it is missing."""
+    """Load libssmscan.so (built in-tree by build.py). Raises if it is missing.
+
+    torch is imported first: PyTorch for ROCm ships its own HIP runtime (SONAME
+    libamdhip64.so.7), and the library must bind to that one, the runtime that owns the
+    tensors and streams it is given. Loaded before torch, the library would pull in the
+    system runtime of the same SONAME and torch would then load its own copy as well: two
+    HIP runtimes in one process, and the library's would find no device."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it first "
                            "(python -m selective_state_space_fwd_amd.build)")
+    import torch  # noqa: F401  (binds the library to torch's HIP runtime; see above)
     L = ctypes.CDLL(LIB_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     L.ssm_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp,
