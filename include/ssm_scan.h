@@ -92,6 +92,8 @@ extern "C" {
 #define SSM_ERR_MISALIGNED (-3)  /* a pointer not aligned to its element size */
 #define SSM_ERR_HIP (-4)         /* the HIP runtime refused the launch (no gfx950 device,
                                     bad stream, ...) */
+#define SSM_ERR_SCRATCH_TOO_SMALL (-5) /* an allocation-free entry point: the problem needs
+                                    more workspace than its static device buffer holds */
 
 /*
  * ssm_scan_fwd -- the selective-scan forward described above.

@@ -83,6 +83,33 @@ SSM_API int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const voi
                         int64_t nheads, int64_t headdim, int64_t dstate, int64_t seqlen,
                         void* stream);
 
+/*
+ * ssm_ssd_fwd_noalloc -- ssm_ssd_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.
+ *
+ * The workspace is a static device buffer of SSM_SSD_NOALLOC_SCRATCH_BYTES (32 MiB) inside
+ * the library; each device the library runs on holds its own copy until the process ends.
+ * Arguments, layouts, results and status codes are those of ssm_ssd_fwd, bit for bit; a
+ * problem whose ssm_ssd_workspace_bytes exceeds the buffer returns
+ * SSM_ERR_SCRATCH_TOO_SMALL before any HIP call (the ssd workload of b4, 32 heads of 64
+ * channels, 128 states, 2048 steps needs 7.3 MB). The call allocates nothing: no
+ * hipMalloc, no hipFree, no library routine that allocates. The buffer's device address is
+ * looked up once per device (hipGetSymbolAddress), on the first call on that device.
+ *
+ * Every call on one device shares that device's buffer, and a call leaves its contents
+ * behind (nothing in it needs clearing: each call writes every part it reads). Calls that
+ * may run at the same time on one device -- on different streams, or from different host
+ * threads without ordering -- race on the buffer and must not be issued.
+ */
+#define SSM_SSD_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+
+SSM_API int ssm_ssd_fwd_noalloc(const void* x, const void* dt, const float* A, const void* B,
+                                const void* C, const float* D, const void* z,
+                                const float* dt_bias, const uint8_t* mask, uint32_t flags,
+                                void* out, float* final_state, int64_t batch, int64_t nheads,
+                                int64_t headdim, int64_t dstate, int64_t seqlen, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

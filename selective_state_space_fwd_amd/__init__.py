@@ -39,13 +39,16 @@ SSM_ERR_INVALID_ARG = -1
 SSM_ERR_UNSUPPORTED = -2
 SSM_ERR_MISALIGNED = -3
 SSM_ERR_HIP = -4
+SSM_ERR_SCRATCH_TOO_SMALL = -5
+
+SSM_SSD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 SSM_CKPT_INTERVAL = 512
 
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_strerror", "ssm_scan_abi_version",
             "ssm_scan_debug_wave_combine", "ssm_scan_ckpt_count", "ssm_scan_fwd_ckpt",
             "ssm_scan_fwd_masked", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes",
-            "ssm_ssd_workspace_bytes", "ssm_ssd_fwd")
+            "ssm_ssd_workspace_bytes", "ssm_ssd_fwd", "ssm_ssd_fwd_noalloc")
 
 _lib = None
 
@@ -101,6 +104,9 @@ def lib() -> ctypes.CDLL:
     L.ssm_ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp, vp,
                               i64, i64, i64, i64, i64, i64, vp]
     L.ssm_ssd_fwd.restype = ctypes.c_int
+    L.ssm_ssd_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint32, vp, vp,
+                                      i64, i64, i64, i64, i64, vp]
+    L.ssm_ssd_fwd_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -162,6 +168,14 @@ def ssm_ssd_fwd(x, dt, A, B, C, D, z, dt_bias, mask, flags, out, final_state, wo
     return lib().ssm_ssd_fwd(x, dt, A, B, C, D, z, dt_bias, mask, flags, out, final_state,
                              workspace, workspace_bytes, batch, nheads, headdim, dstate,
                              seqlen, stream)
+
+
+def ssm_ssd_fwd_noalloc(x, dt, A, B, C, D, z, dt_bias, mask, flags, out, final_state, batch,
+                        nheads, headdim, dstate, seqlen, stream) -> int:
+    """Raw C entry point of the allocation-free Mamba-2 forward (its workspace is the
+    library's static device buffer of SSM_SSD_NOALLOC_SCRATCH_BYTES)."""
+    return lib().ssm_ssd_fwd_noalloc(x, dt, A, B, C, D, z, dt_bias, mask, flags, out,
+                                     final_state, batch, nheads, headdim, dstate, seqlen, stream)
 
 
 def _ptr(t) -> Optional[int]:

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libssmscan.so")
 PROBE_SOURCE = os.path.join(PKG, "probes", "alu_probe.hip")
 PROBE_LIB_PATH = os.path.join(PKG, "libssmprobe.so")
 SOURCES = ["scan_kernels.hip", "scan_short.hip", "scan_bwd.hip", "ssd_kernels.hip", "scan_api.cpp",
-           "ssd_api.cpp"]
+           "ssd_api.cpp", "ssd_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -22,7 +22,7 @@ using ssm_api::span;
 
 extern "C" {
 
-int ssm_scan_abi_version(void) { return 4; }
+int ssm_scan_abi_version(void) { return 5; }
 
 const char* ssm_scan_strerror(int status) {
   switch (status) {
@@ -38,6 +38,9 @@ const char* ssm_scan_strerror(int status) {
       return "a pointer is not aligned to its element size";
     case SSM_ERR_HIP:
       return "the HIP runtime refused the launch";
+    case SSM_ERR_SCRATCH_TOO_SMALL:
+      return "the problem needs more workspace than the allocation-free entry point's static "
+             "device buffer holds (use the entry point that takes a workspace)";
     default:
       return "unknown status";
   }

@@ -145,6 +145,22 @@ struct SsdArgs {
 };
 
 int launch_ssd_fwd(const SsdArgs& a, void* stream);
+
+// A workspace the library owns: the allocation-free entry point's static device buffer.
+// get() returns its device address on the current device (nullptr if the runtime refuses).
+struct SsdScratch {
+  int64_t max_bytes;
+  void* (*get)();
+};
+
+// Every check of ssm_ssd_fwd, then the launch. With `scratch`, the workspace arguments are
+// ignored and the workspace is scratch->get(), called only after every check has passed;
+// a problem needing more than scratch->max_bytes returns SSM_ERR_SCRATCH_TOO_SMALL.
+int ssd_fwd_impl(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* dt_bias, const uint8_t* mask,
+                 uint32_t flags, void* out, float* final_state, void* workspace,
+                 int64_t workspace_bytes, int64_t batch, int64_t nheads, int64_t headdim,
+                 int64_t dstate, int64_t seqlen, void* stream, const SsdScratch* scratch);
 int launch_debug_wave_combine(const float* a, const float* b, float* a_out, float* b_out,
                               int64_t groups, void* stream);
 

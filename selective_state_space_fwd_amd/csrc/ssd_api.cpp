@@ -37,11 +37,15 @@ int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t nheads, int64_t dstate,
   return total;
 }
 
-int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
-                const float* D, const void* z, const float* dt_bias, const uint8_t* mask,
-                uint32_t flags, void* out, float* final_state, void* workspace,
-                int64_t workspace_bytes, int64_t batch, int64_t nheads, int64_t headdim,
-                int64_t dstate, int64_t seqlen, void* stream) {
+}  // extern "C"
+
+namespace ssm {
+
+int ssd_fwd_impl(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* dt_bias, const uint8_t* mask,
+                 uint32_t flags, void* out, float* final_state, void* workspace,
+                 int64_t workspace_bytes, int64_t batch, int64_t nheads, int64_t headdim,
+                 int64_t dstate, int64_t seqlen, void* stream, const SsdScratch* scratch) {
   const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
   if (flags & ~known) return SSM_ERR_INVALID_ARG;
   if (batch < 0 || nheads < 0 || headdim < 0 || dstate < 0 || seqlen < 0)
@@ -70,16 +74,20 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
     return SSM_ERR_UNSUPPORTED;
 
   const bool any = elems > 0;
-  if ((any && (!x || !dt || !out || !workspace)) || (bc > 0 && (!B || !C)) ||
+  if ((any && (!x || !dt || !out || (!workspace && !scratch))) || (bc > 0 && (!B || !C)) ||
       (nheads > 0 && !A))
     return SSM_ERR_INVALID_ARG;
-  if (any && workspace_bytes < need) return SSM_ERR_INVALID_ARG;
+  if (scratch) {
+    if (need > scratch->max_bytes) return SSM_ERR_SCRATCH_TOO_SMALL;
+  } else if (any && workspace_bytes < need) {
+    return SSM_ERR_INVALID_ARG;
+  }
   if (initial_state && state > 0 && !final_state) return SSM_ERR_INVALID_ARG;
 
   if (!aligned(x, 2) || !aligned(dt, 2) || !aligned(B, 2) || !aligned(C, 2) ||
       !aligned(out, 2) || (z && !aligned(z, 2)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
       (dt_bias && !aligned(dt_bias, 4)) || (final_state && !aligned(final_state, 16)) ||
-      !aligned(workspace, 256))
+      (!scratch && !aligned(workspace, 256)))
     return SSM_ERR_MISALIGNED;
 
   if (any) {
@@ -91,7 +99,7 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
         (dt_bias && overlaps(o, span(dt_bias, nheads * 4))) ||
         (mask && overlaps(o, span(mask, batch * seqlen))) ||
         (final_state && overlaps(o, span(final_state, state * 4))) ||
-        overlaps(o, span(workspace, need)))
+        (!scratch && overlaps(o, span(workspace, need))))
       return SSM_ERR_INVALID_ARG;
   }
 
@@ -101,6 +109,13 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
     if (final_state && !initial_state)
       return ssm::launch_fill_zero(final_state, state, stream) == 0 ? SSM_OK : SSM_ERR_HIP;
     return SSM_OK;
+  }
+
+  // Every check has passed: only now may the workspace come from the static scratch
+  // buffer (its address is looked up with a HIP call on first use on a device).
+  if (scratch) {
+    workspace = scratch->get();
+    if (!workspace) return SSM_ERR_HIP;
   }
 
   ssm::SsdArgs a;
@@ -126,6 +141,20 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, co
   a.vec_ok = seqlen % 8 == 0 && aligned(x, 16) && aligned(out, 16) && aligned(B, 16) &&
              aligned(C, 16) && (!z || aligned(z, 16));
   return ssm::launch_ssd_fwd(a, stream) == 0 ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace ssm
+
+extern "C" {
+
+int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                const float* D, const void* z, const float* dt_bias, const uint8_t* mask,
+                uint32_t flags, void* out, float* final_state, void* workspace,
+                int64_t workspace_bytes, int64_t batch, int64_t nheads, int64_t headdim,
+                int64_t dstate, int64_t seqlen, void* stream) {
+  return ssm::ssd_fwd_impl(x, dt, A, B, C, D, z, dt_bias, mask, flags, out, final_state,
+                           workspace, workspace_bytes, batch, nheads, headdim, dstate, seqlen,
+                           stream, nullptr);
 }
 
 }  // extern "C"

@@ -51,17 +51,24 @@ def test_exports_nothing_else():
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("SSM_IO_F32", "SSM_IO_BF16", "SSM_DELTA_SOFTPLUS", "SSM_INITIAL_STATE",
+                 "SSM_WAVES_PER_CHANNEL_1", "SSM_WAVES_PER_CHANNEL_2",
                  "SSM_OK", "SSM_ERR_INVALID_ARG", "SSM_ERR_UNSUPPORTED", "SSM_ERR_MISALIGNED",
-                 "SSM_ERR_HIP"):
+                 "SSM_ERR_HIP", "SSM_ERR_SCRATCH_TOO_SMALL"):
         m = re.search(rf"#define {name} \(?(-?\d+)u?(?: << (\d+))?\)?", text)
         assert m, name
         v = int(m.group(1)) << int(m.group(2) or 0)
         assert getattr(ssm, name) == v, name
 
 
+def test_noalloc_scratch_size_matches_binding():
+    text = open(os.path.join(INCLUDE, "ssm_ssd.h")).read()
+    m = re.search(r"#define SSM_SSD_NOALLOC_SCRATCH_BYTES \(\(int64_t\)(\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == ssm.SSM_SSD_NOALLOC_SCRATCH_BYTES
+
+
 def test_abi_version_and_strerror():
-    assert ssm.ssm_scan_abi_version() == 4
-    for s in (0, -1, -2, -3, -4, 17):
+    assert ssm.ssm_scan_abi_version() == 5
+    for s in (0, -1, -2, -3, -4, -5, 17):
         assert isinstance(ssm.ssm_scan_strerror(s), str) and ssm.ssm_scan_strerror(s)
 
 
@@ -117,12 +124,11 @@ def test_empty_is_a_noop():
 
 
 def test_launch_hints_pass_validation():
-    # each hint alone is a valid flag: the call gets past every check (here, with no device,
-    # it then fails at the launch or at the empty-shape early return)
+    # each hint alone is a valid flag: an empty problem with it is a no-op (no launch)
     for f in (ssm.SSM_WAVES_PER_CHANNEL_1, ssm.SSM_WAVES_PER_CHANNEL_2,
               ssm.SSM_WAVES_PER_CHANNEL_1 | ssm.SSM_IO_BF16):
         assert call(flags=f, batch=0) == ssm.SSM_OK
-        assert call(flags=f) in (ssm.SSM_OK, ssm.SSM_ERR_HIP)
+        assert call(flags=f, dim=0) == ssm.SSM_OK
     with pytest.raises(ValueError):
         ssm._hint_flags(3)
 
@@ -247,6 +253,53 @@ def test_ssd_empty_is_a_noop():
     assert ssd_call(batch=0) == ssm.SSM_OK
     assert ssd_call(nheads=0, A=None) == ssm.SSM_OK
     assert ssd_call(seqlen=0, flags=BF | ssm.SSM_INITIAL_STATE, final_state=FIN) == ssm.SSM_OK
+
+
+def ssd_noalloc_call(**kw):
+    args = dict(x=X, dt=DT, A=A, B=B, C=C, D=None, z=None, dt_bias=None, mask=None, flags=BF,
+                out=OUT, final_state=None, batch=2, nheads=2, headdim=32, dstate=64, seqlen=64,
+                stream=None)
+    args.update(kw)
+    return ssm.ssm_ssd_fwd_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(dt=None), dict(A=None), dict(B=None), dict(out=None), dict(batch=-1),
+    dict(flags=BF | (1 << 9)), dict(flags=BF | ssm.SSM_INITIAL_STATE), dict(out=X),
+    dict(out=B + 64),
+])
+def test_ssd_noalloc_invalid_arguments(kw):
+    """The allocation-free entry point checks exactly what ssm_ssd_fwd checks (no workspace
+    argument to check), with the same codes, before any HIP call."""
+    assert ssd_noalloc_call(**kw) == ssm.SSM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(flags=ssm.SSM_IO_F32), dict(dstate=96), dict(headdim=40)])
+def test_ssd_noalloc_unsupported(kw):
+    assert ssd_noalloc_call(**kw) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_ssd_noalloc_rejects_problems_past_its_buffer():
+    """A problem whose workspace exceeds the static buffer is refused with its own code,
+    before any HIP call; the size check sits on the exact boundary."""
+    cap = ssm.SSM_SSD_NOALLOC_SCRATCH_BYTES
+    # 128 states, 32 heads: 24 KB + 32 KB per (batch row, 64-step block)
+    per_block = ssm.ssm_ssd_workspace_bytes(1, 32, 128, 64)
+    fits = cap // per_block
+    assert ssm.ssm_ssd_workspace_bytes(1, 32, 128, 64 * fits) <= cap
+    assert ssm.ssm_ssd_workspace_bytes(1, 32, 128, 64 * (fits + 1)) > cap
+    big = dict(batch=1, nheads=32, headdim=64, dstate=128, seqlen=64 * (fits + 1))
+    assert ssd_noalloc_call(**big) == ssm.SSM_ERR_SCRATCH_TOO_SMALL
+    assert ssd_noalloc_call(**{**big, "seqlen": 64 * fits, "batch": 0}) == ssm.SSM_OK
+    # the ssd workload (b4, 32 x 64 channels, 128 states, 2048 steps) fits
+    assert ssm.ssm_ssd_workspace_bytes(4, 32, 128, 2048) <= cap
+    assert "static device buffer" in ssm.ssm_scan_strerror(ssm.SSM_ERR_SCRATCH_TOO_SMALL)
+
+
+def test_ssd_noalloc_empty_is_a_noop():
+    assert ssd_noalloc_call(batch=0) == ssm.SSM_OK
+    assert ssd_noalloc_call(seqlen=0, flags=BF | ssm.SSM_INITIAL_STATE,
+                            final_state=FIN) == ssm.SSM_OK
 
 
 def test_probe_library_exports_and_validates():
