@@ -51,7 +51,8 @@ const char* ssm_scan_strerror(int status) {
 namespace {
 
 int64_t ckpt_count(int64_t seqlen) {
-  return seqlen <= 0 ? 0 : (seqlen + SSM_CKPT_INTERVAL - 1) / SSM_CKPT_INTERVAL;
+  // ceil(seqlen / interval), without forming seqlen + interval - 1 (overflows near INT64_MAX)
+  return seqlen <= 0 ? 0 : seqlen / SSM_CKPT_INTERVAL + (seqlen % SSM_CKPT_INTERVAL != 0);
 }
 
 int fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,

@@ -15,7 +15,10 @@ using ssm_api::span;
 
 namespace {
 
-int64_t nblocks_of(int64_t seqlen) { return (seqlen + ssm::kSsdBlock - 1) / ssm::kSsdBlock; }
+// ceil(seqlen / block), without forming seqlen + block - 1 (overflows near INT64_MAX)
+int64_t nblocks_of(int64_t seqlen) {
+  return seqlen / ssm::kSsdBlock + (seqlen % ssm::kSsdBlock != 0);
+}
 
 }  // namespace
 
@@ -28,7 +31,8 @@ int64_t ssm_ssd_workspace_bytes(int64_t batch, int64_t nheads, int64_t dstate,
   const int64_t q = ssm::kSsdBlock;
   // per (batch row, block): G (q x q bf16) and C^T (q x dstate bf16); per (batch row, head,
   // block): the step record, 4 x q fp32
-  if (!mul_ok(dstate, 2 * q, &per_block) || !mul_ok(batch, nblocks_of(seqlen), &blocks) ||
+  if (!mul_ok(dstate, 2 * q, &per_block) || per_block > INT64_MAX - q * q * 2 ||
+      !mul_ok(batch, nblocks_of(seqlen), &blocks) ||
       !mul_ok(blocks, q * q * 2 + per_block, &shared) ||
       !mul_ok(blocks, nheads, &head_blocks) || !mul_ok(head_blocks, 4 * q * 4, &steps) ||
       shared > INT64_MAX - steps)
@@ -55,11 +59,12 @@ int ssd_fwd_impl(const void* x, const void* dt, const float* A, const void* B, c
   if (headdim < 16 || headdim % 16 != 0) return SSM_ERR_UNSUPPORTED;
   const bool initial_state = (flags & SSM_INITIAL_STATE) != 0;
 
-  int64_t dim, row_elems, elems, bc_row, bc, state, hl, need;
+  int64_t dim, row_elems, elems, bc_row, bc, rows, state, head_steps, hl, need;
   if (!mul_ok(nheads, headdim, &dim) || !mul_ok(dim, seqlen, &row_elems) ||
       !mul_ok(batch, row_elems, &elems) || !mul_ok(dstate, seqlen, &bc_row) ||
-      !mul_ok(batch, bc_row, &bc) || !mul_ok(batch * dim, dstate, &state) ||
-      !mul_ok(batch, nheads * seqlen, &hl))
+      !mul_ok(batch, bc_row, &bc) || !mul_ok(batch, dim, &rows) ||
+      !mul_ok(rows, dstate, &state) || !mul_ok(nheads, seqlen, &head_steps) ||
+      !mul_ok(batch, head_steps, &hl))
     return SSM_ERR_UNSUPPORTED;
   // One batch row of x/z/out and of B/C is addressed with 32-bit byte offsets.
   if (row_elems * 2 >= (int64_t(1) << 31) || bc_row * 2 >= (int64_t(1) << 31) ||
