@@ -23,6 +23,12 @@ PROBE_SOURCE = os.path.join(PKG, "probes", "alu_probe.hip")
 PROBE_LIB_PATH = os.path.join(PKG, "libssmprobe.so")
 SOURCES = ["scan_kernels.hip", "scan_short.hip", "scan_bwd.hip", "ssd_kernels.hip", "scan_api.cpp",
            "ssd_api.cpp", "ssd_noalloc.hip"]
+# A test-only build of the Mamba-1 scan with a second launch shape of the chunked kernel (the
+# same 16 steps per lane, other channels per workgroup and states per LDS stage), which the
+# parity tests run against the oracle and against the default build.
+SHAPE2_LIB_PATH = os.path.join(PKG, "libssmscan_shape2.so")
+SHAPE2_SOURCES = ["scan_kernels.hip", "scan_short.hip", "scan_bwd.hip", "scan_api.cpp"]
+SHAPE2_DEFINES = ["-DSSM_BF16_K=4", "-DSSM_BF16_G=4", "-DSSM_F32_K=2", "-DSSM_F32_G=1"]
 ARCH = "gfx950"
 
 
@@ -36,10 +42,10 @@ def compile_flags() -> list:
             "-fvisibility=hidden", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 
-def _link(sources, target, verbose):
+def _link(sources, target, verbose, extra=()):
     fd, tmp = tempfile.mkstemp(prefix=os.path.basename(target) + ".", suffix=".tmp", dir=PKG)
     os.close(fd)
-    cmd = [hipcc(), *compile_flags(), "-shared", "-o", tmp, *sources]
+    cmd = [hipcc(), *compile_flags(), *extra, "-shared", "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, cwd=PKG, capture_output=True, text=True)
@@ -51,8 +57,11 @@ def _link(sources, target, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Build libssmscan.so (the scan library) and libssmprobe.so (the VALU probes)."""
+    """Build libssmscan.so (the scan library), libssmprobe.so (the VALU probes) and
+    libssmscan_shape2.so (the test-only second launch shape)."""
     _link([PROBE_SOURCE], PROBE_LIB_PATH, verbose)
+    _link([os.path.join(CSRC, s) for s in SHAPE2_SOURCES], SHAPE2_LIB_PATH, verbose,
+          SHAPE2_DEFINES)
     return _link([os.path.join(CSRC, s) for s in SOURCES], LIB_PATH, verbose)
 
 

@@ -18,14 +18,20 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 // a rounded sum is representable), and log1p(e) = log(w) - d / w + O(d^2); replacing d / w
 // by d changes the result by d * e / (1 + e), below 1e-7 relative since log1p(e) >= e ln 2.
 // When w rounds to 1, the result is e exactly. Two transcendentals (exp2, log2).
-// max(x, 0) is taken as (x + |x|) / 2 (exact), folded into an FMA with the correction: a
-// float max would first be canonicalised, one more instruction per call.
+// max(x, 0) is one v_max_f32: written as fmaxf, the compiler first canonicalises x, one
+// more instruction per call. x is the result of an add here, never a signalling NaN; at
+// x = -inf the result is 0 + log1p(0) = 0, and a NaN x propagates through e.
+__device__ __forceinline__ float max0_f(float x) {
+  float r;
+  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 __device__ __forceinline__ float softplus_f(float x) {
   const float e = exp2_hw(-__builtin_fabsf(x) * kLog2e);
   const float w = 1.0f + e;
   const float err = (w - 1.0f) - e;
-  const float twice_pos = x + __builtin_fabsf(x);  // 2 max(x, 0)
-  return __builtin_fmaf(log2_hw(w), kLn2, __builtin_fmaf(0.5f, twice_pos, -err));
+  return max0_f(x) + __builtin_fmaf(log2_hw(w), kLn2, -err);
 }
 
 // y * silu(z) = y * z / (1 + e^-z)
