@@ -73,6 +73,18 @@ struct KParams {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Co-resident waves issue oldest first: the workgroups that share a compute unit then finish
+// one after another, and the last one runs alone at low occupancy at the end of the launch.
+// Giving the waves with more work left the higher priority evens out their progress instead:
+// four bands by the share of the wave's state groups still to run (`left` of `total`).
+__device__ __forceinline__ void set_priority_by_work_left(int left, int total) {
+  const int band = (left * 4 - 1) / total;  // 3: the most left, 0: the least
+  if (band >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (band == 2) __builtin_amdgcn_s_setprio(2);
+  else if (band == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Elem: float (fp32 storage) or uint16_t (bf16 bits).
 // T: steps per lane; K: channels (wavefronts) per workgroup; G: states per LDS stage.
 // kVecRows: every streamed row starts 16-byte aligned and holds whole 16-byte words.
@@ -366,6 +378,7 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
 
     for (int g = 0; g < n_groups; ++g) {
       const int it = c * n_groups + g;
+      set_priority_by_work_left(n_chunks * n_groups - it, n_chunks * n_groups);
       stage_issue(it + 1);  // next stage's loads fly while this one computes
       if (g == 0) {
         // The inputs of this chunk have been read out of LDS (DMA) or consumed from
