@@ -8,12 +8,14 @@ contraction, D skip, silu gate, final state) over one batch of seeded synthetic 
 already resident in HBM. The default workload is a Mamba-1 layer's scan: batch 4, 2048
 channels, 16 states, 2048 steps, bf16 storage, fp32 arithmetic.
 
-Timing: W untimed warm-up calls, then exactly K calls between two device
-synchronisations; each call also sits between its own pair of HIP events on the launch
-stream. Calls rotate over several independent input/output sets whose total size is well
-above the 256 MB Infinity Cache, so every call reads HBM ("cold"). The value is the
-algorithmic bytes of K calls divided by the wall time of the timed region. One JSON line
-is printed on stdout.
+Timing: a device-copy reference first (it also takes the GPU out of its idle clocks), W
+untimed warm-up calls, then exactly K calls back to back between two device
+synchronisations, with one HIP event on the launch stream before the first call and one
+after the last; the roofline's mean time per call is their interval over K. Isolated calls,
+each between its own pair of events, are timed after the timed region. Calls rotate over
+several independent input/output sets whose total size is well above the 256 MB Infinity
+Cache, so every call reads HBM ("cold"). The value is the algorithmic bytes of K calls
+divided by the wall time of the timed region. One JSON line is printed on stdout.
 """
 from __future__ import annotations
 
@@ -177,16 +179,16 @@ def host_description():
 
 def copy_reference(torch) -> dict:
     """Device copy of 512 MiB (torch's copy kernel; source and destination together exceed
-    the Infinity Cache), median of 10 launches between HIP events: the bandwidth a plain
-    streaming kernel reaches on this GPU."""
+    the Infinity Cache), median of 20 launches between HIP events after 10 untimed ones: the
+    bandwidth a plain streaming kernel reaches on this GPU."""
     n = 512 << 20
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    for _ in range(3):
+    for _ in range(10):
         dst.copy_(src)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(10)]
+          for _ in range(20)]
     for a, b in ev:
         a.record()
         dst.copy_(src)
@@ -336,22 +338,43 @@ def forward_roofline(w, set_bytes: int, avg_ms: float, traffic, kernel: str) -> 
 
 
 def timed_launches(launch, steps, warmup, stream, torch):
-    """W untimed calls, then K calls between two synchronisations, each between its own
-    pair of HIP events on the launch stream. Returns (wall seconds, per-call ms array)."""
+    """W untimed calls, then exactly K calls back to back between two synchronisations, with
+    one HIP event on the launch stream before the first and one after the last (events
+    between the calls would stop consecutive launches from overlapping their ends and add
+    their own gaps: about 7 us per call on the layer workload). Then, outside the timed
+    region, up to 50 more calls each between its own pair of events, for the duration of an
+    isolated launch. Returns (wall seconds of the K calls, mean ms per call from the two
+    events, per-call ms of the isolated launches)."""
     for i in range(warmup):
         launch(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
+        launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = start.elapsed_time(end) / steps
+    n_iso = min(steps, 50)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_iso)]
+    for i in range(n_iso):
         ev[i][0].record(stream)
         launch(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, np.array([a.elapsed_time(b) for a, b in ev])
+    return wall, per_call_ms, np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def launch_stats(per_call_ms: float, iso_ms) -> dict:
+    """Per-call times: the mean in the timed stream (its two events over K), and the
+    median, p10 and p90 of isolated launches (each between its own pair of events)."""
+    return {"mean_in_stream": round(per_call_ms * 1e3, 3),
+            "isolated_median": round(float(np.median(iso_ms)) * 1e3, 3),
+            "isolated_p10": round(float(np.percentile(iso_ms, 10)) * 1e3, 3),
+            "isolated_p90": round(float(np.percentile(iso_ms, 90)) * 1e3, 3)}
 
 
 def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
@@ -402,8 +425,7 @@ def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
             raise ssm.SsmScanError(st)
 
     K = args.steps
-    wall, kern_ms = timed_launches(launch, K, args.warmup, stream, torch)
-    avg_ms = float(kern_ms.mean())
+    wall, avg_ms, iso_ms = timed_launches(launch, K, args.warmup, stream, torch)
     achieved = set_bytes / (avg_ms * 1e-3) / 1e9
     alu_achieved = BWD_FLOP_EQ_PER_UPDATE * w.tuples / (avg_ms * 1e-3) / 1e12
     t_alu = BWD_FLOP_EQ_PER_UPDATE * w.tuples / (ALU_PEAK_TFLOPS * 1e12)
@@ -437,10 +459,7 @@ def bench_bwd(args, w, inp, torch, ssm, dev) -> int:
                                         f"workspace of {ws_bytes} bytes, fixed-order sums")},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tuples_per_s": round(w.tuples * K / wall, 1),
-        "kernel_us": {"mean": round(avg_ms * 1e3, 3),
-                      "median": round(float(np.median(kern_ms)) * 1e3, 3),
-                      "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
-                      "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
+        "kernel_us": launch_stats(avg_ms, iso_ms),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
@@ -541,8 +560,7 @@ def bench_ssd(args, w, torch, ssm, dev) -> int:
             raise ssm.SsmScanError(st)
 
     K = args.steps
-    wall, kern_ms = timed_launches(launch, K, args.warmup, stream, torch)
-    avg_ms = float(kern_ms.mean())
+    wall, avg_ms, iso_ms = timed_launches(launch, K, args.warmup, stream, torch)
     achieved = set_bytes / (avg_ms * 1e-3) / 1e9
     flops = ssd_mfma_flops(w)
     t_hbm = set_bytes / (HBM_PEAK_GBS * 1e9)
@@ -574,10 +592,7 @@ def bench_ssd(args, w, torch, ssm, dev) -> int:
                    "initial_state": w.initial_state, "buffer_sets": nsets,
                    "algorithmic_bytes": set_bytes},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "kernel_us": {"mean": round(avg_ms * 1e3, 3),
-                      "median": round(float(np.median(kern_ms)) * 1e3, 3),
-                      "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
-                      "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
+        "kernel_us": launch_stats(avg_ms, iso_ms),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
@@ -774,22 +789,12 @@ def main() -> int:
         if st != 0:
             raise ssm.SsmScanError(st)
 
-    for i in range(args.warmup):
-        launch(i)
-    torch.cuda.synchronize()
-
+    # The copy reference runs first: a few milliseconds of streaming that also take the GPU
+    # out of its idle clock state before the warm-up calls (in a fresh process the first
+    # ~60 calls otherwise run several microseconds slower each).
+    copy = copy_reference(torch)
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        launch(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    wall, avg_ms, iso_ms = timed_launches(launch, K, args.warmup, stream, torch)
 
     warm = None
     if not args.no_warm:
@@ -807,8 +812,6 @@ def main() -> int:
                 "note": "one buffer set reused (reads may hit the Infinity Cache); not the metric"}
 
     value = set_bytes * K / wall / 1e9
-    avg_ms = float(kern_ms.mean())
-    med_ms = float(np.median(kern_ms))
     traffic = load_traffic(args.workload)
     kernel = "scan_short_kernel" if w.seqlen <= SHORT_MAX_SEQLEN else "scan_fwd_kernel"
     roofline = forward_roofline(w, set_bytes, avg_ms, traffic, kernel)
@@ -838,20 +841,17 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "elements_per_s": round(w.elements * K / wall, 1),
         "tuples_per_s": round(w.tuples * K / wall, 1),
-        "kernel_us": {"mean": round(avg_ms * 1e3, 3),
-                      "median": round(med_ms * 1e3, 3),
-                      "p10": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
-                      "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 3)},
-        "per_launch_GBps": {"mean": round(set_bytes / (avg_ms * 1e-3) / 1e9, 2),
-                            "median": round(set_bytes / (med_ms * 1e-3) / 1e9, 2),
-                            "note": "algorithmic bytes over one launch's event time; value is "
-                                    "the whole job's wall clock, gaps between launches included"},
+        "kernel_us": launch_stats(avg_ms, iso_ms),
+        "per_launch_GBps": {"in_stream": round(set_bytes / (avg_ms * 1e-3) / 1e9, 2),
+                            "isolated_median": round(
+                                set_bytes / (float(np.median(iso_ms)) * 1e-3) / 1e9, 2),
+                            "note": "algorithmic bytes over the mean time per call in the timed "
+                                    "stream, and over the median of isolated calls"},
         "roofline": roofline,
         "warm": warm,
     }
-    copy = copy_reference(torch)
     copy["pct_of_copy"] = round(100.0 * value / copy["GBps"], 2)
-    copy["note"] = "value against a plain device copy measured in this run, after the metric"
+    copy["note"] = "value against a plain device copy measured in this run, before the metric"
     result["copy_reference"] = copy
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_baseline_seconds)

@@ -395,13 +395,11 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
         // A bare s_barrier: with a release fence the compiler would wait for the DMA of the
         // next chunk's u and delta at the first barrier after it is issued, exposing its
         // latency once per chunk. The DMA writes only this wave's own lds_in slot, read
-        // after the chunk's last barrier, so it only has to land by then: at the last
-        // group every VMEM operation but the z loads issued after it must have completed.
-        // Commits are LDS writes, complete before every barrier.
-        if (g == n_groups - 1) {
-          if (p.z && half == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlocks) : "memory");
-          else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
+        // after the chunk's last barrier, so it only has to land by then: at the last group
+        // the wave waits for all its vector-memory operations (the DMA, and the z loads of
+        // this group, read after the barrier anyway). Commits are LDS writes, complete
+        // before every barrier.
+        if (g == n_groups - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       } else {
         __syncthreads();
