@@ -28,7 +28,7 @@ from .gen import (
     make_ssd_inputs,
     widen,
 )
-from .compare import RTOL, RTOL_STATE, ParityReport, parity
+from .compare import RTOL, RTOL_STATE, WATCH, ParityReport, parity
 
 __all__ = [
     "WORKLOADS",
@@ -45,4 +45,5 @@ __all__ = [
     "ParityReport",
     "RTOL",
     "RTOL_STATE",
+    "WATCH",
 ]

@@ -17,7 +17,7 @@ import pytest
 import oracle
 import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, host, torch
-from ssm_workloads import RTOL, WORKLOADS, f32_to_bf16_bits, make_inputs, parity, widen
+from ssm_workloads import RTOL, WATCH, WORKLOADS, f32_to_bf16_bits, make_inputs, parity, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,7 @@ def compare(io, got, ref, label):
             assert got.get(k) is None, f"{label}: {k} should be absent"
             continue
         rtol = RTOL[io] if k in PER_ELEMENT else RTOL_F32_OUT
-        rep = parity(got[k], r, rtol)
+        rep = parity(got[k], r, rtol, WATCH[io] if k in PER_ELEMENT else None)
         print(f"[grad] {label} {k}: {rep}", flush=True)
         assert rep.ok, f"{label} {k}: {rep}"
 

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 from gpu_util import announce, run_hip
-from ssm_workloads import (RTOL, RTOL_STATE, WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits,
+from ssm_workloads import (RTOL, WATCH, RTOL_STATE, WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits,
                            make_inputs, parity, widen)
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def _set(inp, key, idx, value):
 
 
 def _check(got, ref, io, label, expect_nonfinite=False):
-    ro, rf = parity(got[0], ref[0], RTOL[io]), parity(got[1], ref[1], RTOL_STATE)
+    ro, rf = parity(got[0], ref[0], RTOL[io], WATCH[io]), parity(got[1], ref[1], RTOL_STATE)
     print(f"[edge] {label}: out {ro} | final {rf}", flush=True)
     assert ro.ok and rf.ok, label
     if expect_nonfinite:

@@ -21,7 +21,7 @@ import pytest
 import oracle
 import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, host, torch
-from ssm_workloads import (RTOL, RTOL_STATE, SSD_WORKLOADS, WORKLOADS, make_inputs,
+from ssm_workloads import (RTOL, WATCH, RTOL_STATE, SSD_WORKLOADS, WORKLOADS, make_inputs,
                            make_ssd_inputs, parity, widen)
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ REPLAYS = 3
 
 
 def check(io, got, ref, label):
-    ro = parity(got[0], ref[0], RTOL[io])
+    ro = parity(got[0], ref[0], RTOL[io], WATCH[io])
     rf = parity(got[1], ref[1], RTOL_STATE)
     print(f"[parity] {label}: out {ro} | final {rf}", flush=True)
     assert ro.ok, f"{label} out: {ro}"

@@ -14,7 +14,7 @@ import pytest
 import oracle
 import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, host, torch
-from ssm_workloads import (RTOL, RTOL_STATE, WORKLOADS, f32_to_bf16_bits, make_inputs,
+from ssm_workloads import (RTOL, WATCH, RTOL_STATE, WORKLOADS, f32_to_bf16_bits, make_inputs,
                            make_mask, parity, widen)
 
 pytestmark = pytest.mark.gpu
@@ -61,7 +61,7 @@ def oracle_fwd(inp, mask, upto=None):
 
 
 def check(io, got, ref, label):
-    ro = parity(got[0], ref[0], RTOL[io])
+    ro = parity(got[0], ref[0], RTOL[io], WATCH[io])
     rf = parity(got[1], ref[1], RTOL_STATE)
     print(f"[parity] {label}: out {ro} | final {rf}", flush=True)
     assert ro.ok, f"{label} out: {ro}"
@@ -181,7 +181,8 @@ def compare_grads(io, got, ref, label):
         if r is None:
             assert got.get(k) is None, f"{label}: {k} should be absent"
             continue
-        rep = parity(got[k], r, RTOL[io] if k in PER_ELEMENT else RTOL_F32_OUT)
+        rep = parity(got[k], r, RTOL[io] if k in PER_ELEMENT else RTOL_F32_OUT,
+                     WATCH[io] if k in PER_ELEMENT else None)
         print(f"[grad] {label} {k}: {rep}", flush=True)
         assert rep.ok, f"{label} {k}: {rep}"
 

@@ -3,7 +3,8 @@ seeded, stored inputs.
 
 Bar (the per-element metric of ssm_workloads.compare):
   * out: rtol 1e-4 for float32 storage; 2e-2 for bfloat16 storage (bf16 output rounding
-    included);
+    included), and for bf16 also the tighter regression watch 2^-8 (1 + 1e-4) + 1e-4, which
+    a float32 result within 1e-4 keeps after rounding to bf16;
   * final_state (always float32, never rounded to bf16): rtol 1e-4.
 Small and medium cases compare every element; the full-size workloads compare a seeded
 sample of rows (plus the first and last) that the oracle computes one by one, in the
@@ -14,7 +15,8 @@ import pytest
 
 import oracle
 from gpu_util import announce, run_hip
-from ssm_workloads import RTOL, RTOL_STATE, WORKLOADS, f32_to_bf16_bits, make_inputs, parity, widen
+from ssm_workloads import (RTOL, RTOL_STATE, WATCH, WORKLOADS, f32_to_bf16_bits, make_inputs,
+                           parity, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +31,7 @@ def oracle_full(inp, softplus=True, use_D=True, use_z=True, use_bias=True):
 
 
 def assert_parity(io, got_out, got_fin, ref_out, ref_fin, label):
-    ro = parity(got_out, ref_out, RTOL[io])
+    ro = parity(got_out, ref_out, RTOL[io], WATCH[io])
     rf = parity(got_fin, ref_fin, RTOL_STATE)
     print(f"[parity] {label}: out {ro} | final {rf}", flush=True)
     assert ro.ok, f"{label} out: {ro}"

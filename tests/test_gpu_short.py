@@ -15,7 +15,7 @@ import pytest
 import oracle
 import selective_state_space_fwd_amd as ssm
 from gpu_util import announce, dev, host, run_hip, torch
-from ssm_workloads import RTOL, RTOL_STATE, WORKLOADS, make_inputs, parity, widen
+from ssm_workloads import RTOL, WATCH, RTOL_STATE, WORKLOADS, make_inputs, parity, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def oracle_full(inp, softplus=True, use_D=True, use_z=True, use_bias=True):
 
 
 def check(io, got, ref, label):
-    ro = parity(got[0], ref[0], RTOL[io])
+    ro = parity(got[0], ref[0], RTOL[io], WATCH[io])
     rf = parity(got[1], ref[1], RTOL_STATE)
     print(f"[parity] {label}: out {ro} | final {rf}", flush=True)
     assert ro.ok, f"{label} out: {ro}"

@@ -1,7 +1,8 @@
 """Host checks of the seeded workload generator and the parity metric."""
 import numpy as np
 
-from ssm_workloads import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs, parity
+from ssm_workloads import (RTOL, WATCH, WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
+                           parity)
 
 
 def test_bf16_round_nearest_even():
@@ -43,3 +44,25 @@ def test_parity_metric():
     rep = parity(r + np.array([0, 0, 1e-3, 0]), r, 1e-4)
     assert not rep.ok and rep.worst_index == (2,)
     assert not parity(np.array([np.nan, 1.0]), np.array([0.0, 1.0]), 1.0).ok
+
+
+def test_bf16_watch_is_the_rounding_bound():
+    """The bf16 regression watch against what rounding alone does.
+
+    An exact result rounded to nearest-even bf16, and the same with a float32-sized error
+    added before rounding, stay within the watch; a result whose rounding error is doubled
+    (one more unit in the last place where the rounding went one way) does not, though it
+    stays within the 2e-2 bar.
+    """
+    rng = np.random.default_rng(77)
+    r = rng.standard_normal(200_000) * np.exp(rng.uniform(-6, 6, 200_000))
+    rounded = bf16_bits_to_f32(f32_to_bf16_bits(r.astype(np.float32)))
+    assert parity(rounded, r, RTOL["bf16"], WATCH["bf16"]).ok
+    noisy = r * (1 + rng.uniform(-5e-5, 5e-5, r.size))
+    rn = bf16_bits_to_f32(f32_to_bf16_bits(noisy.astype(np.float32)))
+    assert parity(rn, r, RTOL["bf16"], WATCH["bf16"]).ok
+    doubled = r + 2.0 * (rounded - r)
+    rep = parity(doubled, r, RTOL["bf16"], WATCH["bf16"])
+    assert rep.err <= RTOL["bf16"] and not rep.ok
+    assert parity(doubled, r, RTOL["bf16"]).ok  # without the watch it would pass
+    assert WATCH["f32"] == RTOL["f32"]
