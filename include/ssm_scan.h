@@ -126,7 +126,7 @@ SSM_API int ssm_scan_fwd(const void* u, const void* delta, const float* A, const
 
 /* Saved states sit every SSM_CKPT_INTERVAL steps: entry k is the state entering step
  * k * SSM_CKPT_INTERVAL (entry 0 is the initial state). */
-#define SSM_CKPT_INTERVAL 512
+#define SSM_CKPT_INTERVAL 256
 
 /* Number of saved states per (batch row, channel): ceil(seqlen / SSM_CKPT_INTERVAL), 0 for
  * seqlen <= 0. */
@@ -188,8 +188,9 @@ SSM_API int ssm_scan_fwd_masked(const void* u, const void* delta, const float* A
  * are accumulated with floating-point atomics (after a zero fill), which needs no scratch but
  * is slower and not reproducible from run to run (within fp32 rounding of one another); du,
  * ddelta, dz and dh0 are reproducible either way. Errors as for ssm_scan_fwd, plus
- * SSM_ERR_INVALID_ARG for a workspace that is too small or overlaps an argument and
- * SSM_ERR_MISALIGNED for one not 256-byte aligned.
+ * SSM_ERR_INVALID_ARG for a workspace that is too small or overlaps an argument,
+ * SSM_ERR_MISALIGNED for one not 256-byte aligned, and SSM_ERR_UNSUPPORTED for a row of
+ * seqlen elements above 1 GiB (two channel rows are addressed as one 2 GiB block).
  */
 SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
                          const void* C, const float* D, const void* z,
@@ -202,9 +203,8 @@ SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const
 
 /*
  * Bytes of workspace ssm_scan_bwd needs for reproducible sums: each workgroup's sums of dB
- * and dC over its channels (16 channels per workgroup for bf16 storage, 8 for fp32, set by
- * the storage type in flags bits 0-1), 2 x dstate x seqlen fp32 per workgroup, and dA, dD
- * and dbias per batch row. 0 for empty problems; -1 for negative sizes, an unknown storage
+ * and dC over its channels (32 channels per workgroup, whatever the storage type in flags
+ * bits 0-1), 2 x dstate x seqlen fp32 per workgroup, and dA, dD and dbias per batch row. 0 for empty problems; -1 for negative sizes, an unknown storage
  * type or a size past int64.
  */
 SSM_API int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate,
@@ -213,7 +213,7 @@ SSM_API int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t
 /* Static, human-readable text for a status code (never NULL). */
 SSM_API const char* ssm_scan_strerror(int status);
 
-/* Version of this ABI (bumped on any incompatible change): 3. */
+/* Version of this ABI (bumped on any incompatible change): 6. */
 SSM_API int ssm_scan_abi_version(void);
 
 /*

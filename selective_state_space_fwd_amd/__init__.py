@@ -43,7 +43,7 @@ SSM_ERR_SCRATCH_TOO_SMALL = -5
 
 SSM_SSD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
-SSM_CKPT_INTERVAL = 512
+SSM_CKPT_INTERVAL = 256
 
 EXPORTED = ("ssm_scan_fwd", "ssm_scan_strerror", "ssm_scan_abi_version",
             "ssm_scan_debug_wave_combine", "ssm_scan_ckpt_count", "ssm_scan_fwd_ckpt",
@@ -320,7 +320,7 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: boo
 def scan_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus: bool = False,
                h0=None, mask=None, waves_per_channel=None):
     """``scan`` that also returns the states the backward pass restarts from:
-    (out, final_state, chunk_states [batch, dim, ceil(seqlen / 512), dstate] float32)."""
+    (out, final_state, chunk_states [batch, dim, ceil(seqlen / 256), dstate] float32)."""
     return _forward(u, delta, A, B, C, D, z, delta_bias, delta_softplus, h0, None, None, True,
                     True, mask, waves_per_channel)
 
@@ -434,7 +434,7 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                    ) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Differentiable selective scan: (out, final_state) as ``scan``, with gradients for u,
     delta, A, B, C, D, z, delta_bias and h0 through autograd. The forward keeps the state
-    every 512 steps (``scan_train``); the backward restarts the scan from them
+    every 256 steps (``scan_train``); the backward restarts the scan from them
     (``scan_backward``, reproducible workspace sums). mask is not differentiable."""
     return _selective_scan_function().apply(u, delta, A, B, C, D, z, delta_bias, h0, mask,
                                             bool(delta_softplus))

@@ -22,7 +22,7 @@ using ssm_api::span;
 
 extern "C" {
 
-int ssm_scan_abi_version(void) { return 5; }
+int ssm_scan_abi_version(void) { return 6; }
 
 const char* ssm_scan_strerror(int status) {
   switch (status) {
@@ -49,6 +49,8 @@ const char* ssm_scan_strerror(int status) {
 }  // extern "C"
 
 namespace {
+
+static_assert(ssm::kCkptInterval == SSM_CKPT_INTERVAL, "one saved-state spacing");
 
 int64_t ckpt_count(int64_t seqlen) {
   // ceil(seqlen / interval), without forming seqlen + interval - 1 (overflows near INT64_MAX)
@@ -221,7 +223,8 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
     return SSM_ERR_UNSUPPORTED;
   if (rows > kInt32Max || seqlen > kInt32Max || dim > kInt32Max || rows / 64 + 1 > kInt32Max)
     return SSM_ERR_UNSUPPORTED;
-  if (seqlen * esz > (int64_t(1) << 31) || dstate * seqlen * esz > (int64_t(1) << 31))
+  // A wave addresses its two channels' rows as one buffer with 32-bit byte offsets.
+  if (2 * seqlen * esz > (int64_t(1) << 31) || dstate * seqlen * esz > (int64_t(1) << 31))
     return SSM_ERR_UNSUPPORTED;
 
   // required arrays (NULL only when empty)

@@ -11,16 +11,21 @@
 // adjoint runs backwards in time, g_t = c_t + a_{t+1} g_{t+1}. In the pre-multiplied form
 // e_t = a_t g_t it is a linear recurrence read from the right, e_t = a_t e_{t+1} + a_t c_t,
 // so it has the same combine as the forward, (a1,b1) o (a2,b2) = (a2 a1, a2 b1 + b2), with
-// the later step first. A lane folds its steps from the right into one operator, the wave
-// scans those operators from lane 63 down to lane 0, and each lane replays its steps with
-// the adjoint entering from its right, forming per step:
-//   dC_t += dy_t h_t,  dB_t += g_t s_t u_t  (summed over the workgroup's channels in LDS,
-//   then over workgroups: partial sums in a workspace added up in a fixed order by a second
-//   launch, or float atomics when there is no workspace), du_t += g_t s_t B_t,
+// the later step first. A lane folds its steps from the right into one operator, the
+// lanes of a channel scan those operators from the last lane down, and each lane replays
+// its steps with the adjoint entering from its right, forming per step:
+//   dC_t += dy_t h_t,  dB_t += g_t s_t u_t  (summed over channels: first the two of a wave
+//   in registers, then the wave rows of a workgroup in LDS, then the workgroups: partial
+//   sums in a workspace added up in a fixed order by a second launch, or float atomics
+//   when there is no workspace), du_t += g_t s_t B_t,
 //   ds_t += g_t (A a_t h_{t-1} + B_t u_t), dA += g_t a_t s_t h_{t-1}.
-// The mapping is the forward's: a workgroup owns K channels of one batch row, one
-// wavefront per channel, and lane i owns T consecutive steps of a 64*T-step interval; the
-// intervals are processed last to first, carrying the state adjoint between them.
+//
+// Mapping: a wavefront owns two channels of one batch row, one per 32-lane half, and lane
+// i of a half owns T = 8 consecutive steps of a kCkptInterval-step interval (32 x 8 = 256);
+// the intervals are processed last to first, carrying the state adjoint between them. The
+// two halves of a wave scan independently (DPP inside 16-lane rows, then the row pair), and
+// their dB/dC rows are added with one cross-half swap (v_permlane32_swap) before they
+// reach LDS. A workgroup of W waves owns 2 W channels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -61,17 +66,45 @@ struct BParams {
   int partials;
 };
 
-// Inclusive scan from the right: lane i ends with the composition of the operators of
-// lanes i..63, lane 63 applied first: (a, b) <- (a_i a_j, a_i b_j + b_i) for the lanes j
-// to its right.
-//   1. Inside each 16-lane row, four Hillis-Steele steps read the lane k to the right with
-//      DPP row_shl:k (k = 1, 2, 4, 8); a lane whose source is past the row's end is not
-//      written (no bound_ctrl), which is combining with the identity (1, 0).
-//   2. Lane 16 r now holds row r's whole operator. The operators of the rows to the right
-//      of each row are composed from lanes 16, 32 and 48 (read into scalars) and applied
-//      to every lane of the row.
-// gfx950 needs two wait states between a VALU write and a DPP read of the same VGPR.
-__device__ __forceinline__ void wave_scan_from_right(float& a, float& b, int lane) {
+constexpr int kT = 8;                      // steps per lane
+constexpr int kHalfLanes = 32;             // lanes per channel
+constexpr int kMaxStates = 64;             // the C-ABI layer rejects larger dstate
+static_assert(kHalfLanes * kT == kCkptInterval, "one interval per pass of a channel's lanes");
+
+// Inclusive scan inside each 32-lane half, lane 0 of the half earliest, under the forward's
+// combine. Rows (16 lanes) first, by DPP row_shr:1/2/4/8 (a lane whose source lies outside
+// its row is not written: it combines with the identity), then lane 15 of rows 0 and 2 into
+// rows 1 and 3 (row_bcast:15, row_mask 0xa), which does not cross the halves. Only b is
+// complete afterwards (the caller does not need a). Two wait states between a VALU write
+// and a DPP read of the same VGPR, as in the wave64 scan.
+__device__ __forceinline__ void half_scan_inclusive(float& a, float& b) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(a), "+v"(b));
+}
+
+// Inclusive scan from the right inside each 32-lane half: lane i ends with the composition
+// of the operators of lanes i..31 of its half, the last lane applied first:
+// (a, b) <- (a_i a_j, a_i b_j + b_i) for the lanes j to its right.
+//   1. Inside each row, DPP row_shl:1/2/4/8 (a lane whose source is past the row's end is
+//      not written: the identity).
+//   2. Lane 16 and lane 48 now hold the whole operators of rows 1 and 3; rows 0 and 2
+//      compose them in (rows 1 and 3 have nothing to their right inside their half).
+__device__ __forceinline__ void half_scan_from_right(float& a, float& b, bool odd_row) {
   asm volatile(
       "s_nop 1\n\t"
       "v_fmac_f32_dpp %1, %1, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
@@ -87,315 +120,424 @@ __device__ __forceinline__ void wave_scan_from_right(float& a, float& b, int lan
       "v_mul_f32_dpp %0, %0, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
       "s_nop 1"
       : "+v"(a), "+v"(b));
-  // row operators (rows 1..3), composed from the right
-  const float a3 = readlane(a, 48), b3 = readlane(b, 48);
-  const float a2 = readlane(a, 32), b2 = readlane(b, 32);
   const float a1 = readlane(a, 16), b1 = readlane(b, 16);
-  const float s2a = a3, s2b = b3;                                        // rows 3
-  const float s1a = a2 * a3, s1b = __builtin_fmaf(a2, b3, b2);           // rows 2..3
-  const float s0a = a1 * s1a, s0b = __builtin_fmaf(a1, s1b, b1);         // rows 1..3
-  const int row = lane >> 4;
-  float sa = 1.0f, sb = 0.0f;
-  sa = (row == 0) ? s0a : sa;
-  sb = (row == 0) ? s0b : sb;
-  sa = (row == 1) ? s1a : sa;
-  sb = (row == 1) ? s1b : sb;
-  sa = (row == 2) ? s2a : sa;
-  sb = (row == 2) ? s2b : sb;
+  const float a3 = readlane(a, 48), b3 = readlane(b, 48);
+  const bool upper = __lane_id() >= 32;
+  const float sa = odd_row ? 1.0f : (upper ? a3 : a1);
+  const float sb = odd_row ? 0.0f : (upper ? b3 : b1);
   b = __builtin_fmaf(a, sb, b);
   a = a * sa;
 }
 
-// Lane i receives lane i+1's value; lane 63 receives `last` (DPP wave_shl:1).
-__device__ __forceinline__ float shift_down_one(float v, float last) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(last), __float_as_int(v),
-                                                    0x130, 0xf, 0xf, false));
-}
-
-// Sum over the 64 lanes, in every lane: DPP row_shr partial sums inside each row (lane 15
-// of a row ends with the row's sum), then the four row sums.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
-  return (readlane(v, 15) + readlane(v, 31)) + (readlane(v, 47) + readlane(v, 63));
-}
-
-// Sum over the 64 lanes, complete in lane 63: DPP row_shr partial sums inside each row, then
-// row_bcast:15 and row_bcast:31 carry the row totals up (no readlanes).
-__device__ __forceinline__ float wave_sum_to_last(float v) {
+// Sum over each 32-lane half, complete in the half's last lane (31 or 63): DPP row_shr
+// partial sums inside each row, then row 0's and row 2's totals into rows 1 and 3.
+__device__ __forceinline__ float half_sum_to_last(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
   return v;
+}
+
+// Lane i receives lane i+1's value; the last lane of each half receives `last` (the shift
+// taken in every lane first, as above).
+__device__ __forceinline__ float half_shift_down_one(float v, float last, bool half_end) {
+  const float s = __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(last), __float_as_int(v), 0x130, 0xf, 0xf, false));  // wave_shl:1
+  return half_end ? last : s;
+}
+
+// Lane i receives lane i-1's value; the first lane of each half receives `first`. The shift
+// is taken in every lane before the select: written as `half_start ? first : shift(...)`,
+// the shift is evaluated only where it is chosen, i.e. under an exec mask that disables the
+// first lane of each half, and a DPP read from a disabled lane returns nothing.
+__device__ __forceinline__ float half_shift_up_one(float v, float first, bool half_start) {
+  const float s = shift_up_one(v, first);
+  return half_start ? first : s;
+}
+
+// For two values per lane, lo and hi: the first 32 lanes end with lo + (the same lane of
+// the other half's lo), the last 32 with hi + (the other half's hi); either way the first
+// half's value is added to the second's. v_permlane32_swap exchanges the upper 32 lanes of
+// its first operand with the lower 32 lanes of its second.
+__device__ __forceinline__ float sum_halves(float lo, float hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
 
-// kMask: read a padding mask (its own instantiation: the unmasked kernel's register count
-// decides how many waves fit on a SIMD).
-template <typename Elem, int T, int K, bool kVecRows, bool kMask>
-__global__ __launch_bounds__(64 * K, 4) void scan_bwd_kernel(BParams p) {
+// T steps of a lane from a buffer holding the wave's two channel rows back to back. e0:
+// element offset of the lane's first step t0 inside that buffer; `end` the buffer's length
+// in elements: a word (or, element-wise, an element) at or past step L of its row is read
+// at `end`, i.e. as zero, so that it never reaches into the next row.
+template <typename Elem, bool kVecRows>
+__device__ __forceinline__ void load_steps(const Buf& b, uint32_t e0, int t0, int L,
+                                           uint32_t end, float (&v)[kT]) {
   constexpr int kVec = Vec<Elem>::kN;
-  constexpr int kChunk = 64 * T;
-  constexpr int kBlocks = T / kVec;
   constexpr uint32_t kEsz = sizeof(Elem);
-  // LDS pitch of the per-wave dB/dC rows, [wave][step j][lane]: 72 = 8 (mod 64) words, so
-  // the 64 lanes of a flush read (8 steps x 8 lanes) fall on 64 different banks.
-  constexpr int kPitch = 72;
-  static_assert(kChunk == kCkptInterval, "one interval per saved state");
-  static_assert(T % kVec == 0, "whole 16-byte words per lane");
+  if constexpr (kVecRows) {
+#pragma unroll
+    for (int q = 0; q < kT / kVec; ++q) {
+      const uint32_t e = (t0 + q * kVec < L) ? e0 + q * kVec : end;
+      widen_raw16<Elem>(b.load16(e * kEsz), &v[q * kVec]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kT; ++j) {
+      const uint32_t e = (t0 + j < L) ? e0 + j : end;
+      v[j] = (kEsz == 4) ? __uint_as_float(b.load4(4 * e)) : bf16_lo(b.load2(2 * e));
+    }
+  }
+}
 
-  // [state parity][dB / dC][wave][j * kPitch + lane]: each wave writes its own rows (no
-  // atomics); the flush adds the K rows of a step.
-  __shared__ float acc[2][2][K][T * kPitch];
+// The store counterpart: steps at or past L are dropped (written at `end`).
+template <typename Elem, bool kVecRows>
+__device__ __forceinline__ void store_steps(const Buf& b, uint32_t e0, int t0, int L,
+                                            uint32_t end, const float (&v)[kT]) {
+  constexpr int kVec = Vec<Elem>::kN;
+  if constexpr (kVecRows) {
+#pragma unroll
+    for (int q = 0; q < kT / kVec; ++q) {
+      const uint32_t e = (t0 + q * kVec < L) ? e0 + q * kVec : end;
+      if constexpr (sizeof(Elem) == 4) {
+        b.store16(make_uint4(__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                             __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])),
+                  4 * e);
+      } else {
+        b.store16(make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])),
+                  2 * e);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kT; ++j) {
+      const uint32_t e = (t0 + j < L) ? e0 + j : end;
+      if constexpr (sizeof(Elem) == 4)
+        b.store4(__float_as_uint(v[j]), 4 * e);
+      else
+        b.store2(uint16_t(pack_bf16x2(v[j], 0.0f)), 2 * e);
+    }
+  }
+}
+
+// W: waves per workgroup (2 W channels). M: states between workgroup barriers; the LDS
+// rows of dB and dC have 2 M slots, so that one group of M states is written while the
+// previous one is added up. kMask: read a padding mask (its own instantiation: the unmasked
+// kernel's register count decides how many waves fit on a SIMD).
+template <typename Elem, int W, int M, bool kVecRows, bool kMask>
+__global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
+  constexpr int kVec = Vec<Elem>::kN;
+  constexpr int kSteps = kCkptInterval;  // steps per interval
+  constexpr int kSlots = 2 * M;
+  static_assert(kT % kVec == 0, "whole 16-byte words per lane");
+
+  // [slot][dB / dC][wave][four steps]: each wave writes its own row (the sums of its two
+  // channels); the flush adds the W rows of a step in wave order.
+  __shared__ float4 acc[kSlots][2][W][kSteps / 4];
+  // Per (wave, half, state): the state adjoint carried from the interval to the right, and
+  // the running dA sum over the intervals.
+  __shared__ float s_adj[W][2][kMaxStates];
+  __shared__ float s_dA[W][2][kMaxStates];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;         // which of the wave's two channels
+  const int li = lane & 31;         // lane inside the channel
+  const bool half_start = li == 0, half_end = li == kHalfLanes - 1;
+  const bool odd_row = (lane & 16) != 0;
   const int b = blockIdx.x / p.dblocks;
-  const int d = (blockIdx.x - b * p.dblocks) * K + wave;
-  const bool active = d < p.dim;
+  const int d0 = (blockIdx.x - b * p.dblocks) * (2 * W) + 2 * wave;  // the wave's first channel
+  // Uniform, but the compiler computes the clamp with a vector min/max (v_med3): taken back
+  // to a scalar register here, or every buffer descriptor built from it would be treated as
+  // divergent (a waterfall loop around each access).
+  const int rows_here = __builtin_amdgcn_readfirstlane(
+      p.dim - d0 >= 2 ? 2 : (p.dim - d0 > 0 ? p.dim - d0 : 0));
+  const int d = d0 + hf;
+  const bool active = hf < rows_here;
   const int N = p.dstate, L = p.seqlen;
-  const int n_chunks = (L + kChunk - 1) / kChunk;
-  const int64_t row = int64_t(b) * p.dim + (active ? d : 0);
+  const int n_chunks = (L + kSteps - 1) / kSteps;
+  const int64_t row0 = int64_t(b) * p.dim + (rows_here > 0 ? d0 : 0);
+  const int64_t row = row0 + hf;  // this half's channel (meaningful when active)
 
-  const uint32_t row_bytes = active ? uint32_t(L) * kEsz : 0u;
-  const Buf u_buf(static_cast<const Elem*>(p.u) + row * L, row_bytes);
-  const Buf dl_buf(static_cast<const Elem*>(p.delta) + row * L, row_bytes);
-  const Buf do_buf(static_cast<const Elem*>(p.dout) + row * L, row_bytes);
-  const Buf z_buf(static_cast<const Elem*>(p.z ? p.z : p.u) + row * L, p.z ? row_bytes : 0u);
-  const Buf du_buf(static_cast<Elem*>(p.du) + row * L, row_bytes);
-  const Buf dd_buf(static_cast<Elem*>(p.ddelta) + row * L, row_bytes);
-  const Buf dz_buf(static_cast<Elem*>(p.z ? p.dz : p.du) + row * L, p.z ? row_bytes : 0u);
+  // The wave's channel rows, back to back: lane (hf, li) reads element hf * L + t.
+  const uint32_t end = uint32_t(rows_here) * uint32_t(L);  // elements
+  const uint32_t bytes = end * uint32_t(sizeof(Elem));
+  const Buf u_buf(static_cast<const Elem*>(p.u) + row0 * L, bytes);
+  const Buf dl_buf(static_cast<const Elem*>(p.delta) + row0 * L, bytes);
+  const Buf do_buf(static_cast<const Elem*>(p.dout) + row0 * L, bytes);
+  const Buf z_buf(static_cast<const Elem*>(p.z ? p.z : p.u) + row0 * L, p.z ? bytes : 0u);
+  const Buf du_buf(static_cast<Elem*>(p.du) + row0 * L, bytes);
+  const Buf dd_buf(static_cast<Elem*>(p.ddelta) + row0 * L, bytes);
+  const Buf dz_buf(static_cast<Elem*>(p.z ? p.dz : p.du) + row0 * L, p.z ? bytes : 0u);
   const uint32_t bc_elems = uint32_t(N) * uint32_t(L);
-  const Buf B_buf(static_cast<const Elem*>(p.B) + int64_t(b) * N * L, bc_elems * kEsz);
-  const Buf C_buf(static_cast<const Elem*>(p.C) + int64_t(b) * N * L, bc_elems * kEsz);
+  const Buf B_buf(static_cast<const Elem*>(p.B) + int64_t(b) * N * L, bc_elems * sizeof(Elem));
+  const Buf C_buf(static_cast<const Elem*>(p.C) + int64_t(b) * N * L, bc_elems * sizeof(Elem));
+  const uint32_t row_e = uint32_t(hf) * uint32_t(L);  // this half's row inside the buffers
 
-  // Per-state values live in lane n of these registers.
-  float A_l = 0.0f, gc_l = 0.0f, dA_l = 0.0f, Dd = 0.0f, bias_d = 0.0f;
-  if (active) {
-    Dd = p.D ? p.D[d] : 0.0f;
-    bias_d = p.bias ? p.bias[d] : 0.0f;
-    if (lane < N) {
-      A_l = p.A[int64_t(d) * N + lane];
-      if (p.dfinal) gc_l = p.dfinal[row * N + lane];  // e_{L-1} = dfinal
-    }
+  const float Dd = (active && p.D) ? p.D[d] : 0.0f;
+  const float bias_d = (active && p.bias) ? p.bias[d] : 0.0f;
+  for (int n = li; n < N; n += kHalfLanes) {
+    s_adj[wave][hf][n] = (active && p.dfinal) ? p.dfinal[row * N + n] : 0.0f;  // e_{L-1}
+    s_dA[wave][hf][n] = 0.0f;
   }
-  const float a2_l = A_l * kLog2e;
-  float dD_acc = 0.0f, db_acc = 0.0f;
+  {
+    // slots of inactive waves are read by the flush: they stay zero
+    float4* flat = &acc[0][0][0][0];
+    for (int i = tid; i < kSlots * 2 * W * (kSteps / 4); i += 64 * W)
+      flat[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  __syncthreads();
+
   // Where the flush adds this workgroup's dB and dC rows: this batch row of the outputs, or
   // this workgroup's slot of partial sums. Both take the same offset (state, step) after it.
   const int64_t nl = int64_t(N) * L;
   float* const flush0 = p.partials ? p.dB + int64_t(blockIdx.x) * 2 * nl : p.dB + b * nl;
   float* const flush1 = p.partials ? flush0 + nl : p.dC + b * nl;
-
-  {
-    // rows of inactive waves are read by the flush: they stay zero
-    float* flat = &acc[0][0][0][0];
-    for (int i = tid; i < 2 * 2 * K * T * kPitch; i += 64 * K) flat[i] = 0.0f;
-  }
-  __syncthreads();
-
-  // B or C words of state n for this lane's steps (zeros past the end of the sequence).
-  auto load_bc = [&](const Buf& buf, int n, int tb, float (&v)[T]) {
-#pragma unroll
-    for (int q = 0; q < kBlocks; ++q) {
-      const int t0 = tb + q * kVec;
-      const uint32_t e = (t0 < L) ? uint32_t(n) * uint32_t(L) + uint32_t(t0) : bc_elems;
-      widen_raw16<Elem>(load_word<Elem, kVecRows>(buf, e), &v[q * kVec]);
+  const int total = n_chunks * N;  // (interval, state) pairs, in processing order
+  // Adds the workgroup's rows of the pairs first .. first + count - 1 into dB and dC: one
+  // (pair, gradient, step) item per thread and pass. (c0, n0): the interval and state of
+  // pair `first`; the pairs after it take the next states, then the interval to the left.
+  auto flush = [&](int first, int count, int c0, int n0) {
+    for (int i = tid; i < count * 2 * kSteps; i += 64 * W) {
+      const int k = i / (2 * kSteps);
+      const int wc = (i / kSteps) & 1;  // 0: dB, 1: dC
+      const int st = i % kSteps;
+      const int pair = first + k;
+      int c = c0, n = n0 + k;
+      while (n >= N) {
+        n -= N;
+        --c;
+      }
+      const int t = c * kSteps + st;
+      const float* src = reinterpret_cast<const float*>(&acc[pair % kSlots][wc][0][0]) + st;
+      float v = 0.0f;
+#pragma unroll 4
+      for (int w = 0; w < W; ++w) v += src[w * kSteps];
+      if (t < L) {
+        float* dst = (wc ? flush1 : flush0) + (int64_t(n) * L + t);
+        if (p.partials)
+          *dst = v;
+        else
+          unsafeAtomicAdd(dst, v);
+      }
     }
   };
 
-  int it = 0;  // states processed so far: selects the LDS buffer
+  // A and the saved state of an (interval, state) pair, fetched one pair ahead of their use
+  // (c < 0: past the last pair, read as zero). Both through the wave's rows as one buffer,
+  // a per-half offset in a register and the pair's part uniform (a per-lane 64-bit address
+  // would hold two registers each across the state loop).
+  const uint32_t a_bytes = uint32_t(rows_here * N) * 4u;
+  const uint32_t ck_bytes = uint32_t(rows_here * p.n_ckpt * N) * 4u;
+  const Buf A_buf(p.A + int64_t(rows_here > 0 ? d0 : 0) * N, a_bytes);
+  const Buf ck_buf(p.ckpt + row0 * p.n_ckpt * N, ck_bytes);
+  const uint32_t a_off = uint32_t(hf * N) * 4u, ck_off = uint32_t(hf * p.n_ckpt * N) * 4u;
+  auto fetch_pair = [&](int c, int n, float& A_out, float& h_out) {
+    A_out = __uint_as_float(A_buf.load4(c >= 0 ? a_off + uint32_t(n) * 4u : a_bytes));
+    h_out = __uint_as_float(ck_buf.load4(c >= 0 ? ck_off + uint32_t(c * N + n) * 4u : ck_bytes));
+  };
+  float A_nx, hc_nx;
+  fetch_pair(n_chunks - 1, 0, A_nx, hc_nx);
+
+  float dD_acc = 0.0f, db_acc = 0.0f;
+  int pair = 0;
+  int grp_c = n_chunks - 1, grp_n = 0;  // the current group's first pair
   for (int c = n_chunks - 1; c >= 0; --c) {
-    const int tb = c * kChunk + lane * T;
-    float uv[T], sv[T], xv[T], dyv[T], gdu[T], gds[T];
+    const int t0 = c * kSteps + li * kT;
+    const uint32_t e0 = row_e + uint32_t(t0);
+    // Live across the state loop: s, s u, dL/dy, y and the two sums over the states (u
+    // itself is read again after the loop).
+    float su[kT], sv[kT], dyv[kT], y[kT], gdu[kT], gds[kT];
     float sdt = 0.0f;
-    uint32_t pad_bits = 0;  // bit j: step tb + j is padding (masked kernels only)
+    uint32_t pad_bits = 0;  // bit j: step t0 + j is padding (masked kernels only)
     {
-      float dov[T], zv[T];
+      float uv[kT], xv[kT], dov[kT], zv[kT];
+      load_steps<Elem, kVecRows>(u_buf, e0, t0, L, end, uv);
+      load_steps<Elem, kVecRows>(dl_buf, e0, t0, L, end, xv);
+      load_steps<Elem, kVecRows>(do_buf, e0, t0, L, end, dov);
+      load_steps<Elem, kVecRows>(z_buf, e0, t0, L, end, zv);
 #pragma unroll
-      for (int q = 0; q < kBlocks; ++q) {
-        const uint32_t e = uint32_t(tb + q * kVec);
-        widen_raw16<Elem>(load_word<Elem, kVecRows>(u_buf, e), &uv[q * kVec]);
-        widen_raw16<Elem>(load_word<Elem, kVecRows>(dl_buf, e), &xv[q * kVec]);
-        widen_raw16<Elem>(load_word<Elem, kVecRows>(do_buf, e), &dov[q * kVec]);
-        widen_raw16<Elem>(load_word<Elem, kVecRows>(z_buf, e), &zv[q * kVec]);
-      }
-#pragma unroll
-      for (int j = 0; j < T; ++j) {
+      for (int j = 0; j < kT; ++j) {
         const float x = xv[j] + bias_d;
         float s = p.softplus ? softplus_f(x) : x;
-        if (tb + j >= L) s = uv[j] = dov[j] = 0.0f;  // past the end: identity steps
+        if (t0 + j >= L || !active) s = uv[j] = dov[j] = zv[j] = 0.0f;  // identity steps
         if constexpr (kMask) {
-          if (tb + j < L && p.mask[int64_t(b) * L + tb + j] == 0) {
+          if (t0 + j < L && p.mask[int64_t(b) * L + t0 + j] == 0) {
             s = 0.0f;  // padding: the state is kept (the step is the identity)
             pad_bits |= 1u << j;
           }
         }
         sv[j] = s;
+        su[j] = s * uv[j];
         sdt += s;
         dyv[j] = dov[j];
       }
-      const float hc_l = (active && lane < N) ? p.ckpt[(row * p.n_ckpt + c) * N + lane] : 0.0f;
-
       // With the gate, dL/dy = dout z sigmoid(z) does not need y; only dL/dz does, and y
       // (before the gate) is summed over the states in the loop below, which recomputes
-      // every h_t anyway. dout, z and the biased step size are read again after the loop
-      // (from L2) rather than kept live across it.
-      float y[T];
+      // every h_t anyway. dout, z and the raw step size are read again after the loop
+      // rather than kept live across it.
 #pragma unroll
-      for (int j = 0; j < T; ++j) y[j] = Dd * uv[j];
+      for (int j = 0; j < kT; ++j) y[j] = Dd * uv[j];
       if (p.z) {
 #pragma unroll
-        for (int j = 0; j < T; ++j) dyv[j] = dov[j] * zv[j] * sigmoid_f(zv[j]);
+        for (int j = 0; j < kT; ++j) dyv[j] = dov[j] * zv[j] * sigmoid_f(zv[j]);
       }
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
+      for (int j = 0; j < kT; ++j) {
         dD_acc = __builtin_fmaf(dyv[j], uv[j], dD_acc);
         gdu[j] = 0.0f;  // sum over states of g B (du and the step size share it)
         gds[j] = 0.0f;  // sum over states of g A a h_{t-1}
       }
+    }
 
-      for (int n = 0; n < N; ++n) {
-        const int par = it & 1;
-        if (active) {
-          const float a2 = readlane(a2_l, n), An = readlane(A_l, n);
-          const float hc = readlane(hc_l, n), G = readlane(gc_l, n);
-          float Bv[T], Cv[T], dA[T], h[T];
-          load_bc(B_buf, n, tb, Bv);
-          load_bc(C_buf, n, tb, Cv);
-          // forward again from the saved state: h_t for this lane's steps
-          float bseg = (lane == 0) ? hc : 0.0f;
+    for (int n = 0; n < N; ++n, ++pair) {
+      const float An = A_nx, hc = hc_nx;
+      const int c_nx = n + 1 < N ? c : c - 1, n_nx = n + 1 < N ? n + 1 : 0;
+      fetch_pair(c_nx, n_nx, A_nx, hc_nx);
+      const float a2 = An * kLog2e;
+      const float G = s_adj[wave][hf][n];  // e entering the interval from the right
+      float Bv[kT], Cv[kT], dA[kT], h[kT];
+      {
+        const uint32_t eb = uint32_t(n) * uint32_t(L) + uint32_t(t0);
 #pragma unroll
-          for (int j = 0; j < T; ++j) {
-            dA[j] = exp2_hw(sv[j] * a2);
-            bseg = __builtin_fmaf(dA[j], bseg, (sv[j] * uv[j]) * Bv[j]);
-          }
-          const float alpha = exp2_hw(sdt * a2);  // product of the lane's a_t
-          float aseg = alpha;
-          wave_scan_inclusive(aseg, bseg);
-          const float hin = shift_up_one(bseg, hc);  // state entering the lane's steps
-          {
-            float hh = hin;
-#pragma unroll
-            for (int j = 0; j < T; ++j) {
-              hh = __builtin_fmaf(dA[j], hh, (sv[j] * uv[j]) * Bv[j]);
-              h[j] = hh;
-              y[j] = __builtin_fmaf(Cv[j], hh, y[j]);  // read only with a gate; a select
-                                                       // per step would cost more
-            }
-          }
-          // adjoint: fold the lane's steps from the right, scan from lane 63 down
-          float beta = 0.0f;
-#pragma unroll
-          for (int j = T - 1; j >= 0; --j) beta = dA[j] * __builtin_fmaf(Cv[j], dyv[j], beta);
-          float ra = alpha, rb = beta;
-          wave_scan_from_right(ra, rb, lane);
-          // lane 63's right neighbour is the next interval: the identity applied to G
-          const float an = shift_down_one(ra, 1.0f), bn = shift_down_one(rb, 0.0f);
-          float v = __builtin_fmaf(an, G, bn);  // e entering from the right
-          const float G_next = __builtin_fmaf(readlane(ra, 0), G, readlane(rb, 0));
-          gc_l = (lane == n) ? G_next : gc_l;
-          float dAn = 0.0f;
-#pragma unroll
-          for (int j = T - 1; j >= 0; --j) {
-            const float g = __builtin_fmaf(Cv[j], dyv[j], v);  // g_t = C_t dy_t + e_{t+1}
-            const float hp = (j > 0) ? h[j - 1] : hin;
-            const float t1 = dA[j] * hp;
-            acc[par][0][wave][j * kPitch + lane] = g * (sv[j] * uv[j]);  // dB
-            acc[par][1][wave][j * kPitch + lane] = dyv[j] * h[j];        // dC
-            const float q = g * t1;
-            gdu[j] = __builtin_fmaf(g, Bv[j], gdu[j]);
-            gds[j] = __builtin_fmaf(q, An, gds[j]);
-            dAn = __builtin_fmaf(q, sv[j], dAn);
-            v = dA[j] * g;  // e_t = a_t g_t
-          }
-          dAn = readlane(wave_sum_to_last(dAn), 63);
-          dA_l = (lane == n) ? dA_l + dAn : dA_l;
+        for (int q = 0; q < kT / kVec; ++q) {
+          const uint32_t e = (t0 + q * kVec < L) ? eb + q * kVec : bc_elems;
+          widen_raw16<Elem>(load_word<Elem, kVecRows>(B_buf, e), &Bv[q * kVec]);
+          widen_raw16<Elem>(load_word<Elem, kVecRows>(C_buf, e), &Cv[q * kVec]);
         }
-        __syncthreads();  // every channel's share of state n is in acc[par]
-        // Add the workgroup's sums for state n into dB and dC: one (gradient, step) item per
-        // thread and pass, dB items first (whole waves take the same gradient). The buffer is
-        // written again two states later, after the next barrier, which no thread passes
-        // before finishing this loop. Every active wave overwrites its rows for every state;
-        // inactive waves' rows stay zero.
-        for (int i = tid; i < 2 * kChunk; i += 64 * K) {
-          const int wc = i >= kChunk ? 1 : 0;  // 0: dB, 1: dC
-          const int st = i - wc * kChunk;
-          const int ln = st / T, j = st - ln * T;
-          const int t = c * kChunk + st;
-          float v = 0.0f;
-#pragma unroll 4  // fully unrolled, the K loads in flight would push past 128 registers
-          for (int k = 0; k < K; ++k) v += acc[par][wc][k][j * kPitch + ln];
-          if (t < L) {
-            float* dst = (wc ? flush1 : flush0) + (int64_t(n) * L + t);
-            if (p.partials)
-              *dst = v;
-            else
-              unsafeAtomicAdd(dst, v);
-          }
-        }
-        ++it;
       }
-      // du_t = s_t sum_n g B + D dy_t and ds_t = sum_n g (A a h_{t-1} + B u_t), from the two
-      // sums over the states.
+      // forward again from the saved state: h_t for this lane's steps
+      float bseg = half_start ? hc : 0.0f;
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
+      for (int j = 0; j < kT; ++j) {
+        dA[j] = exp2_hw(sv[j] * a2);
+        bseg = __builtin_fmaf(dA[j], bseg, su[j] * Bv[j]);
+      }
+      const float alpha = exp2_hw(sdt * a2);  // product of the lane's a_t
+      {
+        float aseg = alpha;
+        half_scan_inclusive(aseg, bseg);  // bseg: the state after the lane's last step
+      }
+      const float hin = half_shift_up_one(bseg, hc, half_start);  // entering the lane's steps
+      {
+        float hh = hin;
+#pragma unroll
+        for (int j = 0; j < kT; ++j) {
+          hh = (j == kT - 1) ? bseg : __builtin_fmaf(dA[j], hh, su[j] * Bv[j]);
+          h[j] = hh;
+          y[j] = __builtin_fmaf(Cv[j], hh, y[j]);  // read only with a gate; a select per
+                                                   // step would cost more
+        }
+      }
+      // adjoint: fold the lane's steps from the right, scan from the half's last lane down
+      float beta = 0.0f;
+#pragma unroll
+      for (int j = kT - 1; j >= 0; --j) beta = dA[j] * __builtin_fmaf(Cv[j], dyv[j], beta);
+      float ra = alpha, rb = beta;
+      half_scan_from_right(ra, rb, odd_row);
+      // the last lane's right neighbour is the next interval: the identity applied to G
+      const float an = half_shift_down_one(ra, 1.0f, half_end);
+      const float bn = half_shift_down_one(rb, 0.0f, half_end);
+      float v = __builtin_fmaf(an, G, bn);  // e entering this lane's steps from the right
+      if (half_start) s_adj[wave][hf][n] = __builtin_fmaf(ra, G, rb);  // into the interval
+                                                                       // to the left
+      // dB and dC rows of the step pairs (j, j + 4) are added across the two halves as
+      // soon as both exist and go to LDS at once: four steps per lane, 8 li + 4 hf on.
+      float dBr[kT / 2], dCr[kT / 2];
+      const int slot = pair % kSlots;
+      float* const rowB = reinterpret_cast<float*>(&acc[slot][0][wave][2 * li + hf]);
+      float* const rowC = reinterpret_cast<float*>(&acc[slot][1][wave][2 * li + hf]);
+      float dAn = 0.0f;
+#pragma unroll
+      for (int j = kT - 1; j >= 0; --j) {
+        const float g = __builtin_fmaf(Cv[j], dyv[j], v);  // g_t = C_t dy_t + e_{t+1}
+        const float hp = (j > 0) ? h[j - 1] : hin;
+        const float q = g * (dA[j] * hp);
+        const float gB = g * su[j], gC = dyv[j] * h[j];
+        if (j >= kT / 2) {
+          dBr[j - kT / 2] = gB;
+          dCr[j - kT / 2] = gC;
+        } else {
+          rowB[j] = sum_halves(gB, dBr[j]);
+          rowC[j] = sum_halves(gC, dCr[j]);
+        }
+        gdu[j] = __builtin_fmaf(g, Bv[j], gdu[j]);
+        gds[j] = __builtin_fmaf(q, An, gds[j]);
+        dAn = __builtin_fmaf(q, sv[j], dAn);
+        v = dA[j] * g;  // e_t = a_t g_t
+      }
+      dAn = half_sum_to_last(dAn);
+      if (half_end) atomicAdd(&s_dA[wave][hf][n], dAn);  // one lane per address: in order
+      if ((pair + 1) % M == 0) {
+        __syncthreads();  // every wave's rows of the group are in acc
+        // The group's slots are written again one group later, after the next barrier,
+        // which no thread passes before finishing this flush.
+        flush(pair + 1 - M, M, grp_c, grp_n);
+        grp_c = c_nx;
+        grp_n = n_nx;
+      }
+    }
+    // du_t = s_t sum_n g B + D dy_t and ds_t = sum_n g (A a h_{t-1} + B u_t), from the two
+    // sums over the states.
+    {
+      float uv[kT];
+      load_steps<Elem, kVecRows>(u_buf, e0, t0, L, end, uv);
+#pragma unroll
+      for (int j = 0; j < kT; ++j) {
         gds[j] = __builtin_fmaf(uv[j], gdu[j], gds[j]);
         gdu[j] = __builtin_fmaf(sv[j], gdu[j], Dd * dyv[j]);
       }
-      if (p.z) {
-        float dz2[T], zz[T];
+    }
+    if (p.z) {
+      float dz2[kT], zz[kT];
+      load_steps<Elem, kVecRows>(do_buf, e0, t0, L, end, dz2);
+      load_steps<Elem, kVecRows>(z_buf, e0, t0, L, end, zz);
 #pragma unroll
-        for (int q = 0; q < kBlocks; ++q) {
-          const uint32_t e = uint32_t(tb + q * kVec);
-          widen_raw16<Elem>(load_word<Elem, kVecRows>(do_buf, e), &dz2[q * kVec]);
-          widen_raw16<Elem>(load_word<Elem, kVecRows>(z_buf, e), &zz[q * kVec]);
-        }
+      for (int j = 0; j < kT; ++j) {
+        const float sg = sigmoid_f(zz[j]);
+        dz2[j] = dz2[j] * y[j] * sg * __builtin_fmaf(zz[j], 1.0f - sg, 1.0f);
+      }
+      store_steps<Elem, kVecRows>(dz_buf, e0, t0, L, end, dz2);
+    }
+    float dd[kT];
+    {
+      float xv[kT];
+      if (p.softplus)  // the raw step size again, for softplus' derivative
+        load_steps<Elem, kVecRows>(dl_buf, e0, t0, L, end, xv);
 #pragma unroll
-        for (int j = 0; j < T; ++j) {
-          const float sg = sigmoid_f(zz[j]);
-          dz2[j] = dz2[j] * y[j] * sg * __builtin_fmaf(zz[j], 1.0f - sg, 1.0f);
+      for (int j = 0; j < kT; ++j) {
+        dd[j] = p.softplus ? gds[j] * sigmoid_f(xv[j] + bias_d) : gds[j];
+        if constexpr (kMask) {
+          if (pad_bits & (1u << j)) dd[j] = 0.0f;  // a padding step's step size is not used
         }
-        store_lane_block<Elem, kVecRows, T>(dz_buf, uint32_t(tb), dz2);
+        if (t0 + j < L) db_acc += dd[j];
       }
     }
-    float dd[T];
-    if (p.softplus) {  // the raw step size again (from L2), for softplus' derivative
-#pragma unroll
-      for (int q = 0; q < kBlocks; ++q)
-        widen_raw16<Elem>(load_word<Elem, kVecRows>(dl_buf, uint32_t(tb + q * kVec)),
-                          &xv[q * kVec]);
-    }
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-      const float x = xv[j] + bias_d;
-      dd[j] = p.softplus ? gds[j] * sigmoid_f(x) : gds[j];
-      if constexpr (kMask) {
-        if (pad_bits & (1u << j)) dd[j] = 0.0f;  // a padding step's step size is not used
-      }
-      if (tb + j < L) db_acc += dd[j];
-    }
-    store_lane_block<Elem, kVecRows, T>(du_buf, uint32_t(tb), gdu);
-    store_lane_block<Elem, kVecRows, T>(dd_buf, uint32_t(tb), dd);
+    store_steps<Elem, kVecRows>(du_buf, e0, t0, L, end, gdu);
+    store_steps<Elem, kVecRows>(dd_buf, e0, t0, L, end, dd);
+  }
+  if (total % M != 0) {  // the last, partly filled group
+    __syncthreads();
+    flush(total - total % M, total % M, grp_c, grp_n);
   }
 
+  const float sD = half_sum_to_last(dD_acc), sb = half_sum_to_last(db_acc);
   if (active) {
-    if (lane < N) {
-      if (p.dh0) p.dh0[row * N + lane] = gc_l;  // e_{-1} = a_0 g_0
+    // s_adj and s_dA were last written by lanes of this wave; LDS keeps a wave's order
+    for (int n = li; n < N; n += kHalfLanes) {
+      const float dAv = s_dA[wave][hf][n];
+      if (p.dh0) p.dh0[row * N + n] = s_adj[wave][hf][n];  // e_{-1} = a_0 g_0
       if (p.partials)
-        p.dA[row * N + lane] = dA_l;
+        p.dA[row * N + n] = dAv;
       else
-        unsafeAtomicAdd(&p.dA[int64_t(d) * N + lane], dA_l);
+        unsafeAtomicAdd(&p.dA[int64_t(d) * N + n], dAv);
     }
-    const float sD = wave_sum(dD_acc), sb = wave_sum(db_acc);
-    if (lane == 0) {
+    if (half_end) {
       if (p.partials) {
         if (p.dD) p.dD[row] = sD;
         if (p.dbias) p.dbias[row] = sb;
@@ -511,7 +653,7 @@ __global__ __launch_bounds__(256) void fill_zero_many_kernel(ZeroList z) {
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
-template <typename Elem, int T, int K>
+template <typename Elem, int W, int M>
 int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   BParams p;
   p.u = a.u;
@@ -538,7 +680,7 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   p.dim = int(a.dim);
   p.dstate = int(a.dstate);
   p.seqlen = int(a.seqlen);
-  p.dblocks = int((a.dim + K - 1) / K);
+  p.dblocks = int((a.dim + 2 * W - 1) / (2 * W));
   p.softplus = a.softplus ? 1 : 0;
   p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
   BwdWorkspace ws{};
@@ -553,17 +695,17 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
     p.dbias = a.dbias ? a.workspace + ws.dbias : nullptr;
   }
   const int64_t blocks = a.batch * p.dblocks;
-  const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * K);
+  const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * W);
   if (a.vec_ok) {
     if (a.mask)
-      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, true, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, true>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, true, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, false>), grid, block, 0, s, p);
   } else {
     if (a.mask)
-      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, false, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, true>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((scan_bwd_kernel<Elem, T, K, false, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, false>), grid, block, 0, s, p);
   }
   int st = int(hipGetLastError());
   if (st != 0 || !a.workspace) return st;
@@ -599,8 +741,8 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
 int launch_scan_bwd(const BwdArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.workspace) {  // partial sums, then the reduction launch overwrites every output
-    if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, kBwdChannelsBf16>(a, s);
-    return launch_bwd_typed<float, 8, kBwdChannelsF32>(a, s);
+    if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, kBwdWavesBf16, kBwdGroup>(a, s);
+    return launch_bwd_typed<float, kBwdWavesF32, kBwdGroup>(a, s);
   }
   // Without a workspace the channel- and batch-summed gradients are accumulated with
   // atomics: zero all five in one launch (five small launches cost more than their bytes).
@@ -624,11 +766,8 @@ int launch_scan_bwd(const BwdArgs& a, void* stream) {
     const int st = int(hipGetLastError());
     if (st != 0) return st;
   }
-  // bf16: 16 channels per workgroup, half the dB/dC atomics of 8 at the same 4 waves per SIMD
-  // (one 16-wave workgroup per CU; its per-wave rows take 144 KB of LDS). fp32 keeps 8: at
-  // 16 its masked kernel spills past 128 registers.
-  if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, 8, kBwdChannelsBf16>(a, s);
-  return launch_bwd_typed<float, 8, kBwdChannelsF32>(a, s);
+  if (a.io == Io::BF16) return launch_bwd_typed<uint16_t, kBwdWavesBf16, kBwdGroup>(a, s);
+  return launch_bwd_typed<float, kBwdWavesF32, kBwdGroup>(a, s);
 }
 
 }  // namespace ssm

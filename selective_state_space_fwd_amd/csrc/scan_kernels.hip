@@ -102,7 +102,8 @@ template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bo
 __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
   constexpr int kVec = Vec<Elem>::kN;          // elements per 16-byte word
   constexpr int kChunk = 64 * T;               // steps per chunk
-  static_assert(kChunk == 2 * kCkptInterval, "checkpoints sit at chunk starts and halves");
+  static_assert(kChunk % kCkptInterval == 0 && kCkptInterval % T == 0,
+                "saved states sit at chunk starts and at lane boundaries inside a chunk");
   constexpr int kQuads = T / 4;                // float4 LDS words per lane per state
   constexpr int kWordsPerState = kChunk / kVec;      // 16-byte words per state per chunk
   constexpr int kGS = G * S;                   // states per stage (G for each wave of a channel)
@@ -247,9 +248,12 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
   // Training forward: this row's saved states, [n_ckpt][N] fp32.
   const Buf ck_buf(kCkpt ? p.ckpt + row * int64_t(p.n_ckpt) * N : nullptr,
                    kCkpt && active ? uint32_t(p.n_ckpt) * uint32_t(N) * 4u : 0u);
-  // The saved state in the middle of a chunk is the state after step kCkptInterval - 1 of
-  // the chunk: the inclusive scan result of the lane whose segment ends there.
-  constexpr int kMidLane = kCkptInterval / T - 1;
+  // The saved states inside a chunk are the states after steps kCkptInterval - 1,
+  // 2 kCkptInterval - 1, ... of the chunk: the inclusive scan results of the lanes whose
+  // segments end there (every kLanesPerCkpt-th lane, except the chunk's last, whose state
+  // is the next chunk's first). Saved state k of the row sits at k * N.
+  constexpr int kLanesPerCkpt = kCkptInterval / T;
+  constexpr int kCkptPerChunk = kChunk / kCkptInterval;
 
   // One state group: the B/C words of stage `it` (chunk c) are in lds_bc[it & 1].
   auto compute_group = [&](int it, int c, int g) {
@@ -289,8 +293,14 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
         hc_lane = writelane(hc_lane, readlane(bseg, 63), n);  // carry into the next chunk
         if constexpr (kCkpt) {
-          if (lane == kMidLane && 2 * c + 1 < p.n_ckpt)
-            ck_buf.store4(__float_as_uint(bseg), uint32_t((2 * c + 1) * N + n) * 4u);
+          // One single-lane store each, at a uniform offset (a per-lane offset would hold a
+          // register across the state loop). Past the last saved state the offset is beyond
+          // the buffer and the store is dropped.
+#pragma unroll
+          for (int m = 1; m < kCkptPerChunk; ++m)
+            if (lane == m * kLanesPerCkpt - 1)
+              ck_buf.store4(__float_as_uint(bseg),
+                            uint32_t((kCkptPerChunk * c + m) * N + n) * 4u);
         }
         // Replay the lane's steps from the carried-in state. The state after the last step
         // is the scan's inclusive result itself.
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
     const int tb = c * kChunk + lane * T;
     sdt = 0.0f;
     if (kCkpt && active && lane < N && own)  // the state entering the chunk
-      ck_buf.store4(__float_as_uint(hc_lane), uint32_t(2 * c * N + lane) * 4u);
+      ck_buf.store4(__float_as_uint(hc_lane), uint32_t(kCkptPerChunk * c * N + lane) * 4u);
     {
       const bool tail = (c + 1) * kChunk > L;
 #pragma unroll

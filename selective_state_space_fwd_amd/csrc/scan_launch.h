@@ -31,7 +31,7 @@ struct FwdArgs {
 
 // Spacing of the saved states that the backward pass restarts from (the state entering
 // steps 0, kCkptInterval, 2 kCkptInterval, ...). Equals SSM_CKPT_INTERVAL in ssm_scan.h.
-constexpr int kCkptInterval = 512;
+constexpr int kCkptInterval = 256;
 
 // Sequences of at most this many steps take the short-sequence kernel (one lane per
 // channel and state, stepping through time); longer ones the chunked scan kernel.
@@ -39,7 +39,7 @@ constexpr int kCkptInterval = 512;
 #define SSM_SHORT_MAX_L 32
 #endif
 constexpr int64_t kShortMaxSeqlen = SSM_SHORT_MAX_L;
-static_assert(SSM_SHORT_MAX_L < 512, "the short kernel saves a single state");
+static_assert(SSM_SHORT_MAX_L < kCkptInterval, "the short kernel saves a single state");
 
 // Each returns a hipError_t value (0 on success).
 int launch_scan_fwd(const FwdArgs& a, void* stream);    // dispatches on seqlen
@@ -77,9 +77,20 @@ struct BwdArgs {
   bool vec_ok;
 };
 
-// Channels (wavefronts) per backward workgroup, by storage type.
-constexpr int kBwdChannelsBf16 = 16;
-constexpr int kBwdChannelsF32 = 8;
+// Wavefronts per backward workgroup, by storage type (two channels per wavefront), and the
+// number of (interval, state) steps between its barriers. One 16-wave workgroup per CU
+// (four waves per SIMD at up to 128 VGPRs).
+#ifndef SSM_BWD_WAVES
+#define SSM_BWD_WAVES 16
+#endif
+#ifndef SSM_BWD_GROUP
+#define SSM_BWD_GROUP 2
+#endif
+constexpr int kBwdWavesBf16 = SSM_BWD_WAVES;
+constexpr int kBwdWavesF32 = SSM_BWD_WAVES;
+constexpr int kBwdGroup = SSM_BWD_GROUP;
+constexpr int kBwdChannelsBf16 = 2 * kBwdWavesBf16;
+constexpr int kBwdChannelsF32 = 2 * kBwdWavesF32;
 
 // The backward's workspace, in floats from its start, every region 256-byte aligned:
 //   part  [batch][groups][2][dstate][seqlen]  each workgroup's sums of dB (0) and dC (1)

@@ -101,7 +101,8 @@ void scan_forward_checks() {
       }
   // the training and masked forms, and the saved-state count
   EXPECT(ssm_scan_ckpt_count(0) == 0 && ssm_scan_ckpt_count(1) == 1 &&
-         ssm_scan_ckpt_count(513) == 2 && ssm_scan_ckpt_count(INT64_MAX) > 0);
+         ssm_scan_ckpt_count(257) == 2 && ssm_scan_ckpt_count(513) == 3 &&
+         ssm_scan_ckpt_count(INT64_MAX) > 0);
   for (int64_t L : kBig) {
     const int st = ssm_scan_fwd_ckpt(at(0), at(1), at<const float>(2), at(3), at(4), nullptr,
                                      nullptr, nullptr, SSM_IO_F32, at(8), at<float>(9),

@@ -67,7 +67,7 @@ def test_noalloc_scratch_size_matches_binding():
 
 
 def test_abi_version_and_strerror():
-    assert ssm.ssm_scan_abi_version() == 5
+    assert ssm.ssm_scan_abi_version() == 6
     for s in (0, -1, -2, -3, -4, -5, 17):
         assert isinstance(ssm.ssm_scan_strerror(s), str) and ssm.ssm_scan_strerror(s)
 
@@ -162,15 +162,15 @@ def bwd_call(**kw):
 
 
 def test_bwd_workspace_size():
-    # bf16: 16 channels per workgroup; fp32: 8. Regions rounded up to 64 floats.
+    # 32 channels per workgroup (16 waves of two). Regions rounded up to 64 floats.
     r64 = lambda x: (x + 63) // 64 * 64
-    for flags, k in ((ssm.SSM_IO_BF16, 16), (ssm.SSM_IO_F32, 8)):
+    for flags, k in ((ssm.SSM_IO_BF16, 32), (ssm.SSM_IO_F32, 32)):
         b, d, n, L = 2, 40, 16, 100
         groups = (d + k - 1) // k
         want = 4 * (r64(b * groups * 2 * n * L) + r64(b * d * n) + 2 * r64(b * d))
         assert ssm.ssm_scan_bwd_workspace_bytes(b, d, n, L, flags) == want
     assert ssm.ssm_scan_bwd_workspace_bytes(4, 2048, 16, 2048, ssm.SSM_IO_BF16) == \
-        4 * (4 * 128 * 2 * 16 * 2048 + 4 * 2048 * 16 + 2 * 4 * 2048)
+        4 * (4 * 64 * 2 * 16 * 2048 + 4 * 2048 * 16 + 2 * 4 * 2048)
     assert ssm.ssm_scan_bwd_workspace_bytes(0, 4, 16, 8, ssm.SSM_IO_BF16) == 0
     assert ssm.ssm_scan_bwd_workspace_bytes(-1, 4, 16, 8, ssm.SSM_IO_BF16) == -1
     assert ssm.ssm_scan_bwd_workspace_bytes(1, 4, 16, 8, 2) == -1

@@ -38,7 +38,7 @@ ro, rf = oracle.scan_ref(widen(inp["u"], "f32"), widen(inp["delta"], "f32"), inp
 po = parity(out.cpu().numpy(), ro, RTOL["f32"])
 pf = parity(fin.cpu().numpy(), rf, RTOL_STATE)
 print("n_ckpt", n, "out", po, "final", pf, flush=True)
-assert n == 2 and po.ok and pf.ok
+assert n == 4 and po.ok and pf.ok
 print("BINDING-OK", flush=True)
 """
 

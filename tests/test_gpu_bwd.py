@@ -85,9 +85,10 @@ def compare(io, got, ref, label):
 
 
 SHAPES = [
-    # (batch, dim, dstate, seqlen): one step, a ragged tail, one and several 512-step
+    # (batch, dim, dstate, seqlen): one step, a ragged tail, one and several 256-step
     # intervals, ragged channel counts, 1 to 64 states
-    (2, 5, 16, 1), (1, 7, 3, 7), (2, 9, 16, 100), (1, 6, 16, 512), (1, 6, 16, 513),
+    (2, 5, 16, 1), (1, 7, 3, 7), (2, 9, 16, 100), (1, 6, 16, 256), (1, 6, 16, 257),
+    (1, 6, 16, 512), (1, 6, 16, 513),
     (2, 5, 4, 1500), (1, 3, 64, 700), (1, 10, 1, 300), (1, 4, 17, 2049),
 ]
 
@@ -134,10 +135,10 @@ def test_saved_states_and_forward_unchanged(io):
     from gpu_util import run_hip
     o2, f2 = run_hip(inp)
     assert np.array_equal(out, o2) and np.array_equal(fin, f2)
-    # entry k is the state entering step 512 k
+    # entry k is the state entering step SSM_CKPT_INTERVAL k
     io_ = inp["io"]
     for k in range(states.shape[2]):
-        t = 512 * k
+        t = ssm.SSM_CKPT_INTERVAL * k
         if t == 0:
             ref = inp["h0"].astype(np.float64)
         else:

@@ -3,7 +3,7 @@
 libssmscan_shape2.so is the Mamba-1 scan built with other compile-time launch parameters:
 4 channels per workgroup and 4 states per LDS stage for bf16 storage (the default build has
 8 and 2), 2 channels per workgroup and 1 state per stage for fp32 (default 4 and 2); both
-keep 16 steps per lane (a 1024-step chunk, two 512-step saved-state intervals). The mapping
+keep 16 steps per lane (a 1024-step chunk, four 256-step saved-state intervals). The mapping
 of channels to workgroups and of states to stages changes; the arithmetic of each state, and
 the order in which y sums the states, do not. With one wave per channel (fp32 forced through
 SSM_WAVES_PER_CHANNEL_1) every output and saved state must therefore be bitwise equal to the
@@ -48,7 +48,7 @@ def run(L, inp, mask=None, ckpt=False):
     n = inp["A"].shape[1]
     out = t.empty_like(g["u"])
     fin = f["h0"].clone() if f["h0"] is not None else t.empty((batch, dim, n), device="cuda")
-    states = t.empty((batch, dim, -(-L_ // 512), n), device="cuda") if ckpt else None
+    states = t.empty((batch, dim, -(-L_ // ssm.SSM_CKPT_INTERVAL), n), device="cuda") if ckpt else None
     m = None if mask is None else t.from_numpy(mask).cuda()
     flags = (ssm.SSM_IO_BF16 if io == "bf16" else ssm.SSM_IO_F32) | ssm.SSM_DELTA_SOFTPLUS
     flags |= ssm.SSM_INITIAL_STATE if f["h0"] is not None else 0

@@ -123,7 +123,7 @@ def test_bool_mask_equals_uint8_mask():
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_masked_saved_states(io):
     """Entry k of the training forward's saved states is the masked state entering step
-    512 k."""
+    SSM_CKPT_INTERVAL k."""
     w, inp = case(2, 6, 16, 1700, io, seed=840)
     mask = make_mask(2, 1700, "random", 841)
     mask[0, 900:] = 0
@@ -139,7 +139,7 @@ def test_masked_saved_states(io):
     assert np.array_equal(host(out), o2) and np.array_equal(host(fin), f2)
     states = host(states)
     for k in range(states.shape[2]):
-        ref = inp["h0"].astype(np.float64) if k == 0 else oracle_fwd(inp, mask, upto=512 * k)[1]
+        ref = inp["h0"].astype(np.float64) if k == 0 else oracle_fwd(inp, mask, upto=ssm.SSM_CKPT_INTERVAL * k)[1]
         rep = parity(states[:, :, k], ref, RTOL_F32_OUT)
         assert rep.ok, f"state {k}: {rep}"
 
