@@ -120,6 +120,14 @@ struct Buf {
   __device__ uint4 load16(uint32_t off) const {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   }
+  // With a uniform part of the offset in a scalar register (soff). Callers keep an access
+  // that must miss the buffer out of range through `off` alone.
+  __device__ uint4 load16(uint32_t off, uint32_t soff) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+  }
+  __device__ uint32_t load4(uint32_t off, uint32_t soff) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+  }
   __device__ uint2 load8(uint32_t off) const {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
   }

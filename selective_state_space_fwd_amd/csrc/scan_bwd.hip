@@ -102,9 +102,12 @@ __device__ __forceinline__ void half_scan_inclusive(float& a, float& b) {
 // (a, b) <- (a_i a_j, a_i b_j + b_i) for the lanes j to its right.
 //   1. Inside each row, DPP row_shl:1/2/4/8 (a lane whose source is past the row's end is
 //      not written: the identity).
-//   2. Lane 16 and lane 48 now hold the whole operators of rows 1 and 3; rows 0 and 2
+//   2. The first lanes of rows 1 and 3 now hold those rows' whole operators; rows 0 and 2
 //      compose them in (rows 1 and 3 have nothing to their right inside their half).
-__device__ __forceinline__ void half_scan_from_right(float& a, float& b, bool odd_row) {
+//      v_permlane16_swap of a register with itself puts row 1 under row 0 and row 3 under
+//      row 2, lane by lane; DPP row_newbcast:0 reads the first lane of that row in every
+//      lane, and row_mask 0x5 writes rows 0 and 2 only.
+__device__ __forceinline__ void half_scan_from_right(float& a, float& b) {
   asm volatile(
       "s_nop 1\n\t"
       "v_fmac_f32_dpp %1, %1, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
@@ -120,13 +123,17 @@ __device__ __forceinline__ void half_scan_from_right(float& a, float& b, bool od
       "v_mul_f32_dpp %0, %0, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
       "s_nop 1"
       : "+v"(a), "+v"(b));
-  const float a1 = readlane(a, 16), b1 = readlane(b, 16);
-  const float a3 = readlane(a, 48), b3 = readlane(b, 48);
-  const bool upper = __lane_id() >= 32;
-  const float sa = odd_row ? 1.0f : (upper ? a3 : a1);
-  const float sb = odd_row ? 0.0f : (upper ? b3 : b1);
-  b = __builtin_fmaf(a, sb, b);
-  a = a * sa;
+  const float na = __uint_as_float(
+      __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false)[1]);
+  const float nb = __uint_as_float(
+      __builtin_amdgcn_permlane16_swap(__float_as_uint(b), __float_as_uint(b), false, false)[1]);
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %3, %0 row_newbcast:0 row_mask:0x5 bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %2, %0 row_newbcast:0 row_mask:0x5 bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(a), "+v"(b)
+      : "v"(na), "v"(nb));
 }
 
 // Sum over each 32-lane half, complete in the half's last lane (31 or 63): DPP row_shr
@@ -249,7 +256,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const int hf = lane >> 5;         // which of the wave's two channels
   const int li = lane & 31;         // lane inside the channel
   const bool half_start = li == 0, half_end = li == kHalfLanes - 1;
-  const bool odd_row = (lane & 16) != 0;
   const int b = blockIdx.x / p.dblocks;
   const int d0 = (blockIdx.x - b * p.dblocks) * (2 * W) + 2 * wave;  // the wave's first channel
   // Uniform, but the compiler computes the clamp with a vector min/max (v_med3): taken back
@@ -302,11 +308,14 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   // Adds the workgroup's rows of the pairs first .. first + count - 1 into dB and dC: one
   // (pair, gradient, step) item per thread and pass. (c0, n0): the interval and state of
   // pair `first`; the pairs after it take the next states, then the interval to the left.
+  // A wave's 64 items share their pair and gradient (64 divides kSteps), so everything but
+  // the step is uniform.
+  static_assert(kSteps % 64 == 0, "a wave's flush items share a pair and a gradient");
   auto flush = [&](int first, int count, int c0, int n0) {
-    for (int i = tid; i < count * 2 * kSteps; i += 64 * W) {
-      const int k = i / (2 * kSteps);
-      const int wc = (i / kSteps) & 1;  // 0: dB, 1: dC
-      const int st = i % kSteps;
+    for (int i0 = 64 * wave; i0 < count * 2 * kSteps; i0 += 64 * W) {
+      const int k = i0 / (2 * kSteps);
+      const int wc = (i0 / kSteps) & 1;  // 0: dB, 1: dC
+      const int st = i0 % kSteps + lane;
       const int pair = first + k;
       int c = c0, n = n0 + k;
       while (n >= N) {
@@ -329,17 +338,17 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   };
 
   // A and the saved state of an (interval, state) pair, fetched one pair ahead of their use
-  // (c < 0: past the last pair, read as zero). Both through the wave's rows as one buffer,
-  // a per-half offset in a register and the pair's part uniform (a per-lane 64-bit address
-  // would hold two registers each across the state loop).
-  const uint32_t a_bytes = uint32_t(rows_here * N) * 4u;
-  const uint32_t ck_bytes = uint32_t(rows_here * p.n_ckpt * N) * 4u;
-  const Buf A_buf(p.A + int64_t(rows_here > 0 ? d0 : 0) * N, a_bytes);
-  const Buf ck_buf(p.ckpt + row0 * p.n_ckpt * N, ck_bytes);
+  // (past the last pair: the first pair again, never used). Both through the wave's rows as
+  // one buffer: the half's offset in a register (an inactive half's lies past the buffer and
+  // reads zero), the pair's part uniform (a per-lane 64-bit address would hold two
+  // registers each across the state loop).
+  const Buf A_buf(p.A + int64_t(rows_here > 0 ? d0 : 0) * N, uint32_t(rows_here * N) * 4u);
+  const Buf ck_buf(p.ckpt + row0 * p.n_ckpt * N, uint32_t(rows_here * p.n_ckpt * N) * 4u);
   const uint32_t a_off = uint32_t(hf * N) * 4u, ck_off = uint32_t(hf * p.n_ckpt * N) * 4u;
   auto fetch_pair = [&](int c, int n, float& A_out, float& h_out) {
-    A_out = __uint_as_float(A_buf.load4(c >= 0 ? a_off + uint32_t(n) * 4u : a_bytes));
-    h_out = __uint_as_float(ck_buf.load4(c >= 0 ? ck_off + uint32_t(c * N + n) * 4u : ck_bytes));
+    if (c < 0) c = n = 0;
+    A_out = __uint_as_float(A_buf.load4(a_off, uint32_t(n) * 4u));
+    h_out = __uint_as_float(ck_buf.load4(ck_off, uint32_t(c * N + n) * 4u));
   };
   float A_nx, hc_nx;
   fetch_pair(n_chunks - 1, 0, A_nx, hc_nx);
@@ -350,6 +359,13 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   for (int c = n_chunks - 1; c >= 0; --c) {
     const int t0 = c * kSteps + li * kT;
     const uint32_t e0 = row_e + uint32_t(t0);
+    // Byte offsets of the lane's B/C words in state 0's row; a word past the sequence's end
+    // is put past the whole buffer, whatever the state row added on top.
+    uint32_t bc_off[kT / kVec];
+#pragma unroll
+    for (int q = 0; q < kT / kVec; ++q)
+      bc_off[q] = (t0 + q * kVec < L) ? uint32_t(t0 + q * kVec) * uint32_t(sizeof(Elem))
+                                      : bc_elems * uint32_t(sizeof(Elem));
     // Live across the state loop: s, s u, dL/dy, y and the two sums over the states (u
     // itself is read again after the loop).
     float su[kT], sv[kT], dyv[kT], y[kT], gdu[kT], gds[kT];
@@ -402,7 +418,15 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       const float a2 = An * kLog2e;
       const float G = s_adj[wave][hf][n];  // e entering the interval from the right
       float Bv[kT], Cv[kT], dA[kT], h[kT];
-      {
+      if constexpr (kVecRows) {
+        // the interval's lane offsets with the state's row as a uniform offset on top
+        const uint32_t srow = uint32_t(n) * uint32_t(L) * uint32_t(sizeof(Elem));
+#pragma unroll
+        for (int q = 0; q < kT / kVec; ++q) {
+          widen_raw16<Elem>(B_buf.load16(bc_off[q], srow), &Bv[q * kVec]);
+          widen_raw16<Elem>(C_buf.load16(bc_off[q], srow), &Cv[q * kVec]);
+        }
+      } else {
         const uint32_t eb = uint32_t(n) * uint32_t(L) + uint32_t(t0);
 #pragma unroll
         for (int q = 0; q < kT / kVec; ++q) {
@@ -439,7 +463,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
 #pragma unroll
       for (int j = kT - 1; j >= 0; --j) beta = dA[j] * __builtin_fmaf(Cv[j], dyv[j], beta);
       float ra = alpha, rb = beta;
-      half_scan_from_right(ra, rb, odd_row);
+      half_scan_from_right(ra, rb);
       // the last lane's right neighbour is the next interval: the identity applied to G
       const float an = half_shift_down_one(ra, 1.0f, half_end);
       const float bn = half_shift_down_one(rb, 0.0f, half_end);
