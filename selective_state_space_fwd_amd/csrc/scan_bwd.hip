@@ -249,6 +249,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   // the running dA sum over the intervals.
   __shared__ float s_adj[W][2][kMaxStates];
   __shared__ float s_dA[W][2][kMaxStates];
+  __shared__ float s_dDb[W][2][2];  // running dD and dbias sums of each channel
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -291,6 +292,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     s_adj[wave][hf][n] = (active && p.dfinal) ? p.dfinal[row * N + n] : 0.0f;  // e_{L-1}
     s_dA[wave][hf][n] = 0.0f;
   }
+  if (li < 2) s_dDb[wave][hf][li] = 0.0f;
   {
     // slots of inactive waves are read by the flush: they stay zero
     float4* flat = &acc[0][0][0][0];
@@ -353,7 +355,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   float A_nx, hc_nx;
   fetch_pair(n_chunks - 1, 0, A_nx, hc_nx);
 
-  float dD_acc = 0.0f, db_acc = 0.0f;
   int pair = 0;
   int grp_c = n_chunks - 1, grp_n = 0;  // the current group's first pair
   for (int c = n_chunks - 1; c >= 0; --c) {
@@ -371,16 +372,24 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     float su[kT], sv[kT], dyv[kT], y[kT], gdu[kT], gds[kT];
     float sdt = 0.0f;
     uint32_t pad_bits = 0;  // bit j: step t0 + j is padding (masked kernels only)
+    float dD_acc = 0.0f;
     {
       float uv[kT], xv[kT], dov[kT], zv[kT];
       load_steps<Elem, kVecRows>(u_buf, e0, t0, L, end, uv);
       load_steps<Elem, kVecRows>(dl_buf, e0, t0, L, end, xv);
       load_steps<Elem, kVecRows>(do_buf, e0, t0, L, end, dov);
       load_steps<Elem, kVecRows>(z_buf, e0, t0, L, end, zv);
+      // the step size: the softplus flag tested once, around the whole loop
+      if (p.softplus) {
+#pragma unroll
+        for (int j = 0; j < kT; ++j) sv[j] = softplus_f(xv[j] + bias_d);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kT; ++j) sv[j] = xv[j] + bias_d;
+      }
 #pragma unroll
       for (int j = 0; j < kT; ++j) {
-        const float x = xv[j] + bias_d;
-        float s = p.softplus ? softplus_f(x) : x;
+        float s = sv[j];
         if (t0 + j >= L || !active) s = uv[j] = dov[j] = zv[j] = 0.0f;  // identity steps
         if constexpr (kMask) {
           if (t0 + j < L && p.mask[int64_t(b) * L + t0 + j] == 0) {
@@ -508,6 +517,9 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     }
     // du_t = s_t sum_n g B + D dy_t and ds_t = sum_n g (A a h_{t-1} + B u_t), from the two
     // sums over the states.
+    // Three phases, each storing its output before the next one's loads are issued (a
+    // memory clobber between them keeps the compiler from hoisting every reload to the top,
+    // which would hold them all live at once).
     {
       float uv[kT];
       load_steps<Elem, kVecRows>(u_buf, e0, t0, L, end, uv);
@@ -516,7 +528,9 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         gds[j] = __builtin_fmaf(uv[j], gdu[j], gds[j]);
         gdu[j] = __builtin_fmaf(sv[j], gdu[j], Dd * dyv[j]);
       }
+      store_steps<Elem, kVecRows>(du_buf, e0, t0, L, end, gdu);
     }
+    asm volatile("" ::: "memory");
     if (p.z) {
       float dz2[kT], zz[kT];
       load_steps<Elem, kVecRows>(do_buf, e0, t0, L, end, dz2);
@@ -528,29 +542,40 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       }
       store_steps<Elem, kVecRows>(dz_buf, e0, t0, L, end, dz2);
     }
-    float dd[kT];
-    {
-      float xv[kT];
-      if (p.softplus)  // the raw step size again, for softplus' derivative
-        load_steps<Elem, kVecRows>(dl_buf, e0, t0, L, end, xv);
+    asm volatile("" ::: "memory");
+    float dd[kT], db_acc = 0.0f;
+    if (p.softplus) {  // the flag tested once, around the whole loop
+      float xv[kT];    // the raw step size again, for softplus' derivative
+      load_steps<Elem, kVecRows>(dl_buf, e0, t0, L, end, xv);
 #pragma unroll
-      for (int j = 0; j < kT; ++j) {
-        dd[j] = p.softplus ? gds[j] * sigmoid_f(xv[j] + bias_d) : gds[j];
-        if constexpr (kMask) {
-          if (pad_bits & (1u << j)) dd[j] = 0.0f;  // a padding step's step size is not used
-        }
-        if (t0 + j < L) db_acc += dd[j];
+      for (int j = 0; j < kT; ++j) dd[j] = gds[j] * sigmoid_f(xv[j] + bias_d);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kT; ++j) dd[j] = gds[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kT; ++j) {
+      if constexpr (kMask) {
+        if (pad_bits & (1u << j)) dd[j] = 0.0f;  // a padding step's step size is not used
+      }
+      if (t0 + j < L) db_acc += dd[j];
+    }
+    store_steps<Elem, kVecRows>(dd_buf, e0, t0, L, end, dd);
+    {
+      // this interval's dD and dbias shares, summed over the half into its last lane
+      const float sD = half_sum_to_last(dD_acc), sb = half_sum_to_last(db_acc);
+      if (half_end) {
+        s_dDb[wave][hf][0] += sD;
+        s_dDb[wave][hf][1] += sb;
       }
     }
-    store_steps<Elem, kVecRows>(du_buf, e0, t0, L, end, gdu);
-    store_steps<Elem, kVecRows>(dd_buf, e0, t0, L, end, dd);
   }
   if (total % M != 0) {  // the last, partly filled group
     __syncthreads();
     flush(total - total % M, total % M, grp_c, grp_n);
   }
 
-  const float sD = half_sum_to_last(dD_acc), sb = half_sum_to_last(db_acc);
+  const float sD = s_dDb[wave][hf][0], sb = s_dDb[wave][hf][1];
   if (active) {
     // s_adj and s_dA were last written by lanes of this wave; LDS keeps a wave's order
     for (int n = li; n < N; n += kHalfLanes) {
