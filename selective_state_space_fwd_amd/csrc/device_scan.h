@@ -149,6 +149,9 @@ struct Buf {
   __device__ void store4(uint32_t v, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
   }
+  __device__ void store4(uint32_t v, uint32_t off, uint32_t soff) const {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, soff, 0);
+  }
   __device__ void store2(uint16_t v, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
   }

@@ -99,7 +99,11 @@ __device__ __forceinline__ void set_priority_by_work_left(int left, int total) {
 // every SIMD two waves. Each wave carries, and saves, the states it scans.
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bool kCkpt,
           bool kMask, int S = 1>
-__global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
+// The bf16 saved-state forms are held to four waves per SIMD (128 VGPRs): unbounded, the
+// saved-state store's per-lane offset takes them two registers past it.
+__global__ __launch_bounds__(64 * K * S)
+__attribute__((amdgpu_waves_per_eu(sizeof(Elem) == 2 && kVecRows && kCkpt ? 4 : 1))) void
+scan_fwd_kernel(KParams p) {
   constexpr int kVec = Vec<Elem>::kN;          // elements per 16-byte word
   constexpr int kChunk = 64 * T;               // steps per chunk
   static_assert(kChunk % kCkptInterval == 0 && kCkptInterval % T == 0,
@@ -254,6 +258,11 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
   // is the next chunk's first). Saved state k of the row sits at k * N.
   constexpr int kLanesPerCkpt = kCkptInterval / T;
   constexpr int kCkptPerChunk = kChunk / kCkptInterval;
+  // Every lane stores its inclusive state at once: the lanes that hold a saved state at
+  // their byte offset (set per chunk), the others far past the buffer, where the range
+  // check drops the store; the state's part of the offset is uniform.
+  const bool ck_lane = lane % kLanesPerCkpt == kLanesPerCkpt - 1 && lane != 63;
+  uint32_t ck_lane_off = 0x80000000u;
 
   // One state group: the B/C words of stage `it` (chunk c) are in lds_bc[it & 1].
   auto compute_group = [&](int it, int c, int g) {
@@ -293,14 +302,8 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
         hc_lane = writelane(hc_lane, readlane(bseg, 63), n);  // carry into the next chunk
         if constexpr (kCkpt) {
-          // One single-lane store each, at a uniform offset (a per-lane offset would hold a
-          // register across the state loop). Past the last saved state the offset is beyond
-          // the buffer and the store is dropped.
-#pragma unroll
-          for (int m = 1; m < kCkptPerChunk; ++m)
-            if (lane == m * kLanesPerCkpt - 1)
-              ck_buf.store4(__float_as_uint(bseg),
-                            uint32_t((kCkptPerChunk * c + m) * N + n) * 4u);
+          // (past the last saved state the offset is beyond the buffer: dropped as well)
+          ck_buf.store4(__float_as_uint(bseg), ck_lane_off, uint32_t(n) * 4u);
         }
         // Replay the lane's steps from the carried-in state. The state after the last step
         // is the scan's inclusive result itself.
@@ -336,6 +339,9 @@ __global__ __launch_bounds__(64 * K * S) void scan_fwd_kernel(KParams p) {
     sdt = 0.0f;
     if (kCkpt && active && lane < N && own)  // the state entering the chunk
       ck_buf.store4(__float_as_uint(hc_lane), uint32_t(kCkptPerChunk * c * N + lane) * 4u);
+    if constexpr (kCkpt)
+      ck_lane_off = ck_lane ? uint32_t((kCkptPerChunk * c + lane / kLanesPerCkpt + 1) * N) * 4u
+                            : 0x80000000u;
     {
       const bool tail = (c + 1) * kChunk > L;
 #pragma unroll
