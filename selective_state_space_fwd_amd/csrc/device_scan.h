@@ -143,6 +143,12 @@ struct Buf {
   __device__ void store16(uint4 v, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
   }
+  // Non-temporal (streaming) store: cache policy bit 1 (nt), for data nothing reads again
+  // soon, so that it does not push out of L2 data that will be.
+  __device__ void store16_nt(uint4 v, uint32_t off) const {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 2);
+  }
   __device__ void store8(uint2 v, uint32_t off) const {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, off, 0, 0);
   }

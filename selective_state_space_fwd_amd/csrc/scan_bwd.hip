@@ -200,7 +200,10 @@ __device__ __forceinline__ void load_steps(const Buf& b, uint32_t e0, int t0, in
   }
 }
 
-// The store counterpart: steps at or past L are dropped (written at `end`).
+// The store counterpart: steps at or past L are dropped (written at `end`). The stores are
+// non-temporal: the gradients are not read again here, and the interval's inputs, read
+// again after its state loop, stay in L2 in their place (reads 244 -> 185 MB per call on
+// the layer workload, with the partial sums' stores non-temporal as well).
 template <typename Elem, bool kVecRows>
 __device__ __forceinline__ void store_steps(const Buf& b, uint32_t e0, int t0, int L,
                                             uint32_t end, const float (&v)[kT]) {
@@ -210,13 +213,13 @@ __device__ __forceinline__ void store_steps(const Buf& b, uint32_t e0, int t0, i
     for (int q = 0; q < kT / kVec; ++q) {
       const uint32_t e = (t0 + q * kVec < L) ? e0 + q * kVec : end;
       if constexpr (sizeof(Elem) == 4) {
-        b.store16(make_uint4(__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
-                             __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])),
-                  4 * e);
+        b.store16_nt(make_uint4(__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                                __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])),
+                     4 * e);
       } else {
-        b.store16(make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])),
-                  2 * e);
+        b.store16_nt(make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])),
+                     2 * e);
       }
     }
   } else {
@@ -331,8 +334,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       for (int w = 0; w < W; ++w) v += src[w * kSteps];
       if (t < L) {
         float* dst = (wc ? flush1 : flush0) + (int64_t(n) * L + t);
-        if (p.partials)
-          *dst = v;
+        if (p.partials)  // read once, by the reduction launch: kept out of L2's way
+          __builtin_nontemporal_store(v, dst);
         else
           unsafeAtomicAdd(dst, v);
       }
