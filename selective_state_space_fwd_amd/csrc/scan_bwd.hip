@@ -288,6 +288,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const Buf B_buf(static_cast<const Elem*>(p.B) + int64_t(b) * N * L, bc_elems * sizeof(Elem));
   const Buf C_buf(static_cast<const Elem*>(p.C) + int64_t(b) * N * L, bc_elems * sizeof(Elem));
   const uint32_t row_e = uint32_t(hf) * uint32_t(L);  // this half's row inside the buffers
+  const Buf mask_buf(kMask ? p.mask + int64_t(b) * L : nullptr, kMask ? uint32_t(L) : 0u);
 
   const float Dd = (active && p.D) ? p.D[d] : 0.0f;
   const float bias_d = (active && p.bias) ? p.bias[d] : 0.0f;
@@ -375,6 +376,14 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     float su[kT], sv[kT], dyv[kT], y[kT], gdu[kT], gds[kT];
     float sdt = 0.0f;
     uint32_t pad_bits = 0;  // bit j: step t0 + j is padding (masked kernels only)
+    // The padding mask of this lane's steps, read branch-free through the batch row's mask
+    // (bytes past the sequence read 1: those steps are identity steps anyway).
+    uint32_t mask_bytes[kT];
+    if constexpr (kMask) {
+#pragma unroll
+      for (int j = 0; j < kT; ++j)
+        mask_bytes[j] = t0 + j < L ? mask_buf.load1(uint32_t(t0 + j)) : 1u;
+    }
     float dD_acc = 0.0f;
     {
       float uv[kT], xv[kT], dov[kT], zv[kT];
@@ -395,8 +404,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         float s = sv[j];
         if (t0 + j >= L || !active) s = uv[j] = dov[j] = zv[j] = 0.0f;  // identity steps
         if constexpr (kMask) {
-          if (t0 + j < L && p.mask[int64_t(b) * L + t0 + j] == 0) {
-            s = 0.0f;  // padding: the state is kept (the step is the identity)
+          if (mask_bytes[j] == 0) {  // padding: the state is kept (the step is the identity)
+            s = 0.0f;
             pad_bits |= 1u << j;
           }
         }
