@@ -105,6 +105,19 @@ def test_backward_shapes(shape, io):
     compare(io, got, run_oracle(inp, dout, dfin, True), w.describe())
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_long_sequence(io):
+    """16 384 steps: the state adjoint carried across 64 intervals of 256 steps, right to left,
+    and the states restarted from 64 saved ones; a channel count that leaves the last
+    workgroup partly empty and its last wave with one channel."""
+    w = WORKLOADS["tiny"].with_(batch=1, dim=37, dstate=16, seqlen=16384, io=io, gate=True,
+                                initial_state=True, a_kind="scaled", seed=640)
+    announce(w.describe() + " backward, long sequence")
+    inp, dout, dfin = setup(w, seed=640)
+    *_, got = run_gpu(inp, dout, dfin, True)
+    compare(io, got, run_oracle(inp, dout, dfin, True), w.describe() + " long")
+
+
 @pytest.mark.parametrize("variant", ["no_D", "no_z", "no_bias", "no_softplus", "no_dfinal",
                                      "bare"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
