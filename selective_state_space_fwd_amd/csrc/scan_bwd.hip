@@ -502,7 +502,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       for (int j = kT - 1; j >= 0; --j) {
         const float g = __builtin_fmaf(Cv[j], dyv[j], v);  // g_t = C_t dy_t + e_{t+1}
         const float hp = (j > 0) ? h[j - 1] : hin;
-        const float q = g * (dA[j] * hp);
+        const float ag = dA[j] * g;  // e_t = a_t g_t, the adjoint entering the step before
+        const float q = ag * hp;     // g_t a_t h_{t-1}
         const float gB = g * su[j], gC = dyv[j] * h[j];
         if (j >= kT / 2) {
           dBr[j - kT / 2] = gB;
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         gdu[j] = __builtin_fmaf(g, Bv[j], gdu[j]);
         gds[j] = __builtin_fmaf(q, An, gds[j]);
         dAn = __builtin_fmaf(q, sv[j], dAn);
-        v = dA[j] * g;  // e_t = a_t g_t
+        v = ag;
       }
       dAn = half_sum_to_last(dAn);
       if (half_end) atomicAdd(&s_dA[wave][hf][n], dAn);  // one lane per address: in order
