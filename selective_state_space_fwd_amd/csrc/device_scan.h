@@ -125,6 +125,11 @@ struct Buf {
   __device__ uint4 load16(uint32_t off, uint32_t soff) const {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
   }
+  // Non-temporal (streaming) load, cache policy bit 1: for a last use, so that the line is
+  // the first to leave L2 and data still to be read again stays.
+  __device__ uint4 load16_nt(uint32_t off) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+  }
   __device__ uint32_t load4(uint32_t off, uint32_t soff) const {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
   }

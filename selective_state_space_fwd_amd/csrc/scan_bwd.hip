@@ -179,8 +179,11 @@ __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_
 // T steps of a lane from a buffer holding the wave's two channel rows back to back. e0:
 // element offset of the lane's first step t0 inside that buffer; `end` the buffer's length
 // in elements: a word (or, element-wise, an element) at or past step L of its row is read
-// at `end`, i.e. as zero, so that it never reaches into the next row.
-template <typename Elem, bool kVecRows>
+// at `end`, i.e. as zero, so that it never reaches into the next row. kLastUse: the
+// interval's second read of an input, after its state loop; streamed (non-temporal), so that
+// its lines leave L2 first and other workgroups' inputs, still to be read again, stay (reads
+// 184 -> 160 MB per call on the layer workload, same time).
+template <typename Elem, bool kVecRows, bool kLastUse = false>
 __device__ __forceinline__ void load_steps(const Buf& b, uint32_t e0, int t0, int L,
                                            uint32_t end, float (&v)[kT]) {
   constexpr int kVec = Vec<Elem>::kN;
@@ -189,7 +192,7 @@ __device__ __forceinline__ void load_steps(const Buf& b, uint32_t e0, int t0, in
 #pragma unroll
     for (int q = 0; q < kT / kVec; ++q) {
       const uint32_t e = (t0 + q * kVec < L) ? e0 + q * kVec : end;
-      widen_raw16<Elem>(b.load16(e * kEsz), &v[q * kVec]);
+      widen_raw16<Elem>(kLastUse ? b.load16_nt(e * kEsz) : b.load16(e * kEsz), &v[q * kVec]);
     }
   } else {
 #pragma unroll
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     // which would hold them all live at once).
     {
       float uv[kT];
-      load_steps<Elem, kVecRows>(u_buf, e0, t0, L, end, uv);
+      load_steps<Elem, kVecRows, true>(u_buf, e0, t0, L, end, uv);
 #pragma unroll
       for (int j = 0; j < kT; ++j) {
         gds[j] = __builtin_fmaf(uv[j], gdu[j], gds[j]);
@@ -546,8 +549,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     asm volatile("" ::: "memory");
     if (p.z) {
       float dz2[kT], zz[kT];
-      load_steps<Elem, kVecRows>(do_buf, e0, t0, L, end, dz2);
-      load_steps<Elem, kVecRows>(z_buf, e0, t0, L, end, zz);
+      load_steps<Elem, kVecRows, true>(do_buf, e0, t0, L, end, dz2);
+      load_steps<Elem, kVecRows, true>(z_buf, e0, t0, L, end, zz);
 #pragma unroll
       for (int j = 0; j < kT; ++j) {
         const float sg = sigmoid_f(zz[j]);
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     float dd[kT], db_acc = 0.0f;
     if (p.softplus) {  // the flag tested once, around the whole loop
       float xv[kT];    // the raw step size again, for softplus' derivative
-      load_steps<Elem, kVecRows>(dl_buf, e0, t0, L, end, xv);
+      load_steps<Elem, kVecRows, true>(dl_buf, e0, t0, L, end, xv);
 #pragma unroll
       for (int j = 0; j < kT; ++j) dd[j] = gds[j] * sigmoid_f(xv[j] + bias_d);
     } else {
