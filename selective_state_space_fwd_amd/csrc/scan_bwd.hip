@@ -256,6 +256,10 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   __shared__ float s_adj[W][2][kMaxStates];
   __shared__ float s_dA[W][2][kMaxStates];
   __shared__ float s_dDb[W][2][2];  // running dD and dbias sums of each channel
+  // B and C of a group's M states over the interval, widened to fp32 once per workgroup
+  // rather than by every wave: [buffer][state in group][B / C][four steps]. Group k reads
+  // buffer k & 1; the rows of group k + 1 go into the other one during group k.
+  __shared__ float4 s_bc[2][M][2][kSteps / 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -314,6 +318,49 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   float* const flush0 = p.partials ? p.dB + int64_t(blockIdx.x) * 2 * nl : p.dB + b * nl;
   float* const flush1 = p.partials ? flush0 + nl : p.dC + b * nl;
   const int total = n_chunks * N;  // (interval, state) pairs, in processing order
+
+  // The staging words: one 16-byte source word per thread of the first kStageWords. The
+  // first M kRowWords threads take B, the next C (a whole number of waves each, so the
+  // array, and with it the buffer descriptor, is uniform in a wave); thread `tid` holds
+  // state-in-group st_ms, steps [st_ws, st_ws + kVec) of the interval. A word at or past
+  // the sequence's end reads zeros (put past the array).
+  constexpr int kRowWords = kSteps / kVec;
+  constexpr int kStageWords = M * 2 * kRowWords;
+  static_assert(kStageWords <= 64 * W, "one staging word per thread");
+  static_assert((M * kRowWords) % 64 == 0, "each array takes whole waves");
+  const bool st_on = wave < kStageWords / 64;
+  const int st_ab = __builtin_amdgcn_readfirstlane(tid / (M * kRowWords));  // 0: B, 1: C
+  const int st_ms = (tid / kRowWords) % M;
+  const int st_ws = (tid % kRowWords) * kVec;
+  auto stage_load = [&](int grp, uint4& st_raw) {  // this thread's word of group grp
+    if (st_on) {
+      const int i0 = grp * M;  // uniform: the group's first (interval, state) pair
+      int c = n_chunks - 1 - i0 / N, n = i0 - (i0 / N) * N + st_ms;
+      while (n >= N) {  // the pairs after it take the next states, then the interval before
+        n -= N;
+        --c;
+      }
+      const int t = c * kSteps + st_ws;
+      const uint32_t e = (c >= 0 && t < L) ? uint32_t(n) * uint32_t(L) + uint32_t(t) : bc_elems;
+      st_raw = load_word<Elem, kVecRows>(st_ab == 0 ? B_buf : C_buf, e);
+    }
+  };
+  auto stage_commit = [&](int grp, const uint4& st_raw) {
+    if (st_on) {
+      float v[kVec];
+      widen_raw16<Elem>(st_raw, v);
+      float4* dst = &s_bc[grp & 1][st_ms][st_ab][st_ws / 4];
+#pragma unroll
+      for (int q = 0; q < kVec / 4; ++q)
+        dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+  };
+  {
+    uint4 w0;
+    stage_load(0, w0);
+    stage_commit(0, w0);
+    __syncthreads();
+  }
   // Adds the workgroup's rows of the pairs first .. first + count - 1 into dB and dC: one
   // (pair, gradient, step) item per thread and pass. (c0, n0): the interval and state of
   // pair `first`; the pairs after it take the next states, then the interval to the left.
@@ -367,13 +414,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   for (int c = n_chunks - 1; c >= 0; --c) {
     const int t0 = c * kSteps + li * kT;
     const uint32_t e0 = row_e + uint32_t(t0);
-    // Byte offsets of the lane's B/C words in state 0's row; a word past the sequence's end
-    // is put past the whole buffer, whatever the state row added on top.
-    uint32_t bc_off[kT / kVec];
-#pragma unroll
-    for (int q = 0; q < kT / kVec; ++q)
-      bc_off[q] = (t0 + q * kVec < L) ? uint32_t(t0 + q * kVec) * uint32_t(sizeof(Elem))
-                                      : bc_elems * uint32_t(sizeof(Elem));
     // Live across the state loop: s, s u, dL/dy, y and the two sums over the states (u
     // itself is read again after the loop).
     float su[kT], sv[kT], dyv[kT], y[kT], gdu[kT], gds[kT];
@@ -433,6 +473,9 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         gdu[j] = 0.0f;  // sum over states of g B (du and the step size share it)
         gds[j] = 0.0f;  // sum over states of g A a h_{t-1}
       }
+      // Formed here: left to the compiler, the sum sinks to its use after the state loop
+      // and keeps u live (and spilled) across it.
+      asm volatile("" : "+v"(dD_acc));
     }
 
     for (int n = 0; n < N; ++n, ++pair) {
@@ -442,21 +485,21 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       const float a2 = An * kLog2e;
       const float G = s_adj[wave][hf][n];  // e entering the interval from the right
       float Bv[kT], Cv[kT], dA[kT], h[kT];
-      if constexpr (kVecRows) {
-        // the interval's lane offsets with the state's row as a uniform offset on top
-        const uint32_t srow = uint32_t(n) * uint32_t(L) * uint32_t(sizeof(Elem));
+      // The next group's rows, fetched at the start of the group's first state and written
+      // into the other buffer before its adjoint part (read only after the group's barrier).
+      // Local to the state, so nothing keeps the word live across the loop.
+      uint4 st_word;
+      {
+        const int grp = pair / M;
+        if (pair % M == 0) stage_load(grp + 1, st_word);
+        const float4* sB = &s_bc[grp & 1][pair % M][0][kT / 4 * li];
 #pragma unroll
-        for (int q = 0; q < kT / kVec; ++q) {
-          widen_raw16<Elem>(B_buf.load16(bc_off[q], srow), &Bv[q * kVec]);
-          widen_raw16<Elem>(C_buf.load16(bc_off[q], srow), &Cv[q * kVec]);
-        }
-      } else {
-        const uint32_t eb = uint32_t(n) * uint32_t(L) + uint32_t(t0);
-#pragma unroll
-        for (int q = 0; q < kT / kVec; ++q) {
-          const uint32_t e = (t0 + q * kVec < L) ? eb + q * kVec : bc_elems;
-          widen_raw16<Elem>(load_word<Elem, kVecRows>(B_buf, e), &Bv[q * kVec]);
-          widen_raw16<Elem>(load_word<Elem, kVecRows>(C_buf, e), &Cv[q * kVec]);
+        for (int q = 0; q < kT / 4; ++q) {
+          const float4 bq = sB[q];
+          Bv[4 * q] = bq.x;
+          Bv[4 * q + 1] = bq.y;
+          Bv[4 * q + 2] = bq.z;
+          Bv[4 * q + 3] = bq.w;
         }
       }
       // forward again from the saved state: h_t for this lane's steps
@@ -467,6 +510,20 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         bseg = __builtin_fmaf(dA[j], bseg, su[j] * Bv[j]);
       }
       const float alpha = exp2_hw(sdt * a2);  // product of the lane's a_t
+      {
+        // C only from here on: read after the recomputation, so its registers are free
+        // during it
+        asm volatile("" ::: "memory");
+        const float4* sC = &s_bc[(pair / M) & 1][pair % M][1][kT / 4 * li];
+#pragma unroll
+        for (int q = 0; q < kT / 4; ++q) {
+          const float4 cq = sC[q];
+          Cv[4 * q] = cq.x;
+          Cv[4 * q + 1] = cq.y;
+          Cv[4 * q + 2] = cq.z;
+          Cv[4 * q + 3] = cq.w;
+        }
+      }
       {
         float aseg = alpha;
         half_scan_inclusive(aseg, bseg);  // bseg: the state after the lane's last step
@@ -482,6 +539,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
                                                    // step would cost more
         }
       }
+      if (pair % M == 0) stage_commit(pair / M + 1, st_word);  // before the adjoint's peak
       // adjoint: fold the lane's steps from the right, scan from the half's last lane down
       float beta = 0.0f;
 #pragma unroll
