@@ -103,11 +103,13 @@ __device__ __forceinline__ void half_scan_inclusive(float& a, float& b) {
 //   1. Inside each row, DPP row_shl:1/2/4/8 (a lane whose source is past the row's end is
 //      not written: the identity).
 //   2. The first lanes of rows 1 and 3 now hold those rows' whole operators; rows 0 and 2
-//      compose them in (rows 1 and 3 have nothing to their right inside their half).
-//      v_permlane16_swap of a register with itself puts row 1 under row 0 and row 3 under
-//      row 2, lane by lane; DPP row_newbcast:0 reads the first lane of that row in every
-//      lane, and row_mask 0x5 writes rows 0 and 2 only.
+//      compose them in (rows 1 and 3 have nothing to their right inside their half). A DPP
+//      wave_shl:1 copy moves lane 16's operator to lane 15 and lane 48's to lane 47 (the
+//      last lanes of rows 0 and 2); DPP row_newbcast:15 reads that lane in every lane of
+//      its row, and row_mask 0x5 writes rows 0 and 2 only.
+// Two wait states between a VALU write and a DPP read of the same VGPR.
 __device__ __forceinline__ void half_scan_from_right(float& a, float& b) {
+  float na, nb;
   asm volatile(
       "s_nop 1\n\t"
       "v_fmac_f32_dpp %1, %1, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
@@ -121,19 +123,14 @@ __device__ __forceinline__ void half_scan_from_right(float& a, float& b) {
       "s_nop 0\n\t"
       "v_fmac_f32_dpp %1, %1, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
       "v_mul_f32_dpp %0, %0, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1"
-      : "+v"(a), "+v"(b));
-  const float na = __uint_as_float(
-      __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false)[1]);
-  const float nb = __uint_as_float(
-      __builtin_amdgcn_permlane16_swap(__float_as_uint(b), __float_as_uint(b), false, false)[1]);
-  asm volatile(
       "s_nop 1\n\t"
-      "v_fmac_f32_dpp %1, %3, %0 row_newbcast:0 row_mask:0x5 bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %0, %2, %0 row_newbcast:0 row_mask:0x5 bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %2, %0 wave_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mov_b32_dpp %3, %1 wave_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %1, %3, %0 row_newbcast:15 row_mask:0x5 bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %0, %2, %0 row_newbcast:15 row_mask:0x5 bank_mask:0xf\n\t"
       "s_nop 1"
-      : "+v"(a), "+v"(b)
-      : "v"(na), "v"(nb));
+      : "+v"(a), "+v"(b), "=&v"(na), "=&v"(nb));
 }
 
 // Sum over each 32-lane half, complete in the half's last lane (31 or 63): DPP row_shr
