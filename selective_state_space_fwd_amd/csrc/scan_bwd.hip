@@ -144,21 +144,20 @@ __device__ __forceinline__ float half_sum_to_last(float v) {
   return v;
 }
 
-// Lane i receives lane i+1's value; the last lane of each half receives `last` (the shift
-// taken in every lane first, as above).
-__device__ __forceinline__ float half_shift_down_one(float v, float last, bool half_end) {
-  const float s = __int_as_float(__builtin_amdgcn_update_dpp(
-      __float_as_int(last), __float_as_int(v), 0x130, 0xf, 0xf, false));  // wave_shl:1
-  return half_end ? last : s;
+// Lane i receives lane i+1's (shift_down_any, DPP wave_shl:1) or lane i-1's (shift_up_any,
+// wave_shr:1) value; what the last (first) lane of each half receives is another channel's
+// value or 0, for callers that select there. Each shift is pinned by an empty asm, so that it
+// is taken in every lane, before the caller's select: moved under the select, it would run
+// with the selected-away lanes disabled, and a DPP read from a disabled lane returns nothing.
+__device__ __forceinline__ float shift_down_any(float v) {
+  float s = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x130, 0xf, 0xf, true));
+  asm volatile("" : "+v"(s));
+  return s;
 }
-
-// Lane i receives lane i-1's value; the first lane of each half receives `first`. The shift
-// is taken in every lane before the select: written as `half_start ? first : shift(...)`,
-// the shift is evaluated only where it is chosen, i.e. under an exec mask that disables the
-// first lane of each half, and a DPP read from a disabled lane returns nothing.
-__device__ __forceinline__ float half_shift_up_one(float v, float first, bool half_start) {
-  const float s = shift_up_one(v, first);
-  return half_start ? first : s;
+__device__ __forceinline__ float shift_up_any(float v) {
+  float s = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x138, 0xf, 0xf, true));
+  asm volatile("" : "+v"(s));
+  return s;
 }
 
 // For two values per lane, lo and hi: the first 32 lanes end with lo + (the same lane of
@@ -525,7 +524,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         float aseg = alpha;
         half_scan_inclusive(aseg, bseg);  // bseg: the state after the lane's last step
       }
-      const float hin = half_shift_up_one(bseg, hc, half_start);  // entering the lane's steps
+      const float up = shift_up_any(bseg);
+      const float hin = half_start ? hc : up;  // the state entering the lane's steps
       {
         float hh = hin;
 #pragma unroll
@@ -543,10 +543,10 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       for (int j = kT - 1; j >= 0; --j) beta = dA[j] * __builtin_fmaf(Cv[j], dyv[j], beta);
       float ra = alpha, rb = beta;
       half_scan_from_right(ra, rb);
-      // the last lane's right neighbour is the next interval: the identity applied to G
-      const float an = half_shift_down_one(ra, 1.0f, half_end);
-      const float bn = half_shift_down_one(rb, 0.0f, half_end);
-      float v = __builtin_fmaf(an, G, bn);  // e entering this lane's steps from the right
+      // e entering this lane's steps from the right; the last lane's right neighbour is the
+      // next interval, whose adjoint G enters unchanged
+      const float an = shift_down_any(ra), bn = shift_down_any(rb);
+      float v = half_end ? G : __builtin_fmaf(an, G, bn);
       if (half_start) s_adj[wave][hf][n] = __builtin_fmaf(ra, G, rb);  // into the interval
                                                                        // to the left
       // dB and dC rows of the step pairs (j, j + 4) are added across the two halves as
