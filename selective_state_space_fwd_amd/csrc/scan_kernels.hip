@@ -98,11 +98,13 @@ __device__ __forceinline__ void set_priority_by_work_left(int left, int total) {
 // hands its share of y to the first through LDS; for launches with too few channels to give
 // every SIMD two waves. Each wave carries, and saves, the states it scans.
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bool kCkpt,
-          bool kMask, int S = 1>
-// The bf16 saved-state forms are held to four waves per SIMD (128 VGPRs): unbounded, the
-// saved-state store's per-lane offset takes them two registers past it.
+          bool kMask, int S = 1, int kN = 0>
+// The bf16 saved-state forms and the unrolled fixed-state form are held to four waves per
+// SIMD (128 VGPRs): unbounded, the saved-state store's per-lane offset, or the unrolled
+// schedule, takes them two registers past it.
 __global__ __launch_bounds__(64 * K * S)
-__attribute__((amdgpu_waves_per_eu(sizeof(Elem) == 2 && kVecRows && kCkpt ? 4 : 1))) void
+__attribute__((amdgpu_waves_per_eu(sizeof(Elem) == 2 && kVecRows && (kCkpt || kN != 0) ? 4 : 1)))
+void
 scan_fwd_kernel(KParams p) {
   constexpr int kVec = Vec<Elem>::kN;          // elements per 16-byte word
   constexpr int kChunk = 64 * T;               // steps per chunk
@@ -122,6 +124,7 @@ scan_fwd_kernel(KParams p) {
   static_assert(kArrayWords % 64 == 0, "each wavefront stages words of one array only");
   static_assert(!kDmaInputs || kVecRows, "input DMA moves whole aligned 16-byte words");
   static_assert(S == 1 || S == 2, "one or two waves per channel");
+  static_assert(kN == 0 || (S == 1 && kN <= 64), "a fixed state count: one wave per channel");
 
   // Staging: [buffer][B=0 / C=1][state-in-group][quad][lane] as float4 (fp32 slots).
   __shared__ float4 lds_bc[2][2][kGS * kQuads * 64];
@@ -138,7 +141,7 @@ scan_fwd_kernel(KParams p) {
   const int b = blockIdx.x / p.dblocks;
   const int d = (blockIdx.x - b * p.dblocks) * K + slot;
   const bool active = d < p.dim;  // a wave past the last channel stages, syncs, stores nothing
-  const int N = p.dstate, L = p.seqlen;
+  const int N = kN ? kN : p.dstate, L = p.seqlen;
   const int64_t row = int64_t(b) * p.dim + (active ? d : 0);
   const uint32_t row_bytes = active ? uint32_t(L) * kEsz : 0u;
 
@@ -159,6 +162,18 @@ scan_fwd_kernel(KParams p) {
     if (lane < N) {
       a2_lane = p.A[int64_t(d) * N + lane] * kLog2e;
       if (p.initial_state) hc_lane = p.final_state[row * N + lane];
+    }
+  }
+
+  // With the state count fixed at compile time, the state loop is unrolled and each state's
+  // A log2(e) and carry live in scalar registers: no readlane of either and no writelane of
+  // the carry per state (the carry is read out of lane 63 straight into its register).
+  float a2_s[kN ? kN : 1], hc_s[kN ? kN : 1];
+  if constexpr (kN != 0) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      a2_s[n] = readlane(a2_lane, n);
+      hc_s[n] = readlane(hc_lane, n);
     }
   }
 
@@ -272,8 +287,14 @@ scan_fwd_kernel(KParams p) {
       const int sl = half * G + nl;  // state within the stage
       const int n = g * kGS + sl;
       if (n < N) {
-        const float a2 = readlane(a2_lane, n);
-        const float hc = readlane(hc_lane, n);
+        float a2, hc;
+        if constexpr (kN != 0) {
+          a2 = a2_s[n];
+          hc = hc_s[n];
+        } else {
+          a2 = readlane(a2_lane, n);
+          hc = readlane(hc_lane, n);
+        }
         const float4* Bq = &lds_bc[buf][0][sl * kQuads * 64 + lane];
         const float4* Cq = &lds_bc[buf][1][sl * kQuads * 64 + lane];
         // All of this state's B words are requested at once, and its C words before the
@@ -300,7 +321,10 @@ scan_fwd_kernel(KParams p) {
         float aseg = exp2_hw(sdt * a2);
         wave_scan_inclusive(aseg, bseg);  // bseg: state at the end of this lane's steps
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
-        hc_lane = writelane(hc_lane, readlane(bseg, 63), n);  // carry into the next chunk
+        if constexpr (kN != 0)  // carry into the next chunk
+          hc_s[n] = readlane(bseg, 63);
+        else
+          hc_lane = writelane(hc_lane, readlane(bseg, 63), n);
         if constexpr (kCkpt) {
           // (past the last saved state the offset is beyond the buffer: dropped as well)
           ck_buf.store4(__float_as_uint(bseg), ck_lane_off, uint32_t(n) * 4u);
@@ -337,6 +361,10 @@ scan_fwd_kernel(KParams p) {
   for (int c = 0; c < n_chunks; ++c) {
     const int tb = c * kChunk + lane * T;
     sdt = 0.0f;
+    if constexpr (kCkpt && kN != 0) {  // the carries, one per lane again, for that store
+#pragma unroll
+      for (int n = 0; n < kN; ++n) hc_lane = writelane(hc_lane, hc_s[n], n);
+    }
     if (kCkpt && active && lane < N && own)  // the state entering the chunk
       ck_buf.store4(__float_as_uint(hc_lane), uint32_t(kCkptPerChunk * c * N + lane) * 4u);
     if constexpr (kCkpt)
@@ -392,7 +420,7 @@ scan_fwd_kernel(KParams p) {
       for (int j = 0; j < T; ++j) sdt += dt[j];
     }
 
-    for (int g = 0; g < n_groups; ++g) {
+    auto group_step = [&](int g) {
       const int it = c * n_groups + g;
       set_priority_by_work_left(n_chunks * n_groups - it, n_chunks * n_groups);
       stage_issue(it + 1);  // next stage's loads fly while this one computes
@@ -420,6 +448,12 @@ scan_fwd_kernel(KParams p) {
       } else {
         __syncthreads();
       }
+    };
+    if constexpr (kN != 0) {
+#pragma unroll
+      for (int g = 0; g < (kN + kGS - 1) / kGS; ++g) group_step(g);
+    } else {
+      for (int g = 0; g < n_groups; ++g) group_step(g);
     }
 
     if constexpr (S == 2) {
@@ -457,6 +491,10 @@ scan_fwd_kernel(KParams p) {
     }
   }
 
+  if constexpr (kN != 0) {
+#pragma unroll
+    for (int n = 0; n < kN; ++n) hc_lane = writelane(hc_lane, hc_s[n], n);
+  }
   if (active && p.final_state && lane < N && own) p.final_state[row * N + lane] = hc_lane;
 }
 
@@ -521,9 +559,23 @@ void launch_flavour(bool ckpt, bool split, dim3 grid, dim3 block, hipStream_t s,
                            block2, 0, s, p);
     }
   } else if (ckpt) {
+    if constexpr (sizeof(Elem) == 2 && kVecRows && !kMask) {
+      if (p.dstate == 16) {
+        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask, 1, 16>),
+                           grid, block, 0, s, p);
+        return;
+      }
+    }
     hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask>), grid, block,
                        0, s, p);
   } else {
+    if constexpr (sizeof(Elem) == 2 && kVecRows && !kMask) {
+      if (p.dstate == 16) {  // 16 states: the unrolled form (the same arithmetic, bit for bit)
+        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask, 1, 16>),
+                           grid, block, 0, s, p);
+        return;
+      }
+    }
     hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask>), grid,
                        block, 0, s, p);
   }
