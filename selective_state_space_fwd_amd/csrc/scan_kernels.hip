@@ -124,7 +124,7 @@ scan_fwd_kernel(KParams p) {
   static_assert(kArrayWords % 64 == 0, "each wavefront stages words of one array only");
   static_assert(!kDmaInputs || kVecRows, "input DMA moves whole aligned 16-byte words");
   static_assert(S == 1 || S == 2, "one or two waves per channel");
-  static_assert(kN == 0 || (S == 1 && kN <= 64), "a fixed state count: one wave per channel");
+  static_assert(kN == 0 || (kN % (G * S) == 0 && kN <= 64), "a fixed state count: whole groups");
 
   // Staging: [buffer][B=0 / C=1][state-in-group][quad][lane] as float4 (fp32 slots).
   __shared__ float4 lds_bc[2][2][kGS * kQuads * 64];
@@ -165,15 +165,18 @@ scan_fwd_kernel(KParams p) {
     }
   }
 
-  // With the state count fixed at compile time, the state loop is unrolled and each state's
-  // A log2(e) and carry live in scalar registers: no readlane of either and no writelane of
-  // the carry per state (the carry is read out of lane 63 straight into its register).
-  float a2_s[kN ? kN : 1], hc_s[kN ? kN : 1];
+  // With the state count fixed at compile time, the state loop is unrolled and each of this
+  // wave's states (own state j is state own_state(j): G of every stage of kGS) keeps its
+  // A log2(e) and carry in scalar registers: no readlane of either and no writelane of the
+  // carry per state (the carry is read out of lane 63 straight into its register).
+  constexpr int kOwnN = kN / S;
+  auto own_state = [&](int j) { return (j / G) * kGS + half * G + j % G; };
+  float a2_s[kN ? kOwnN : 1], hc_s[kN ? kOwnN : 1];
   if constexpr (kN != 0) {
 #pragma unroll
-    for (int n = 0; n < kN; ++n) {
-      a2_s[n] = readlane(a2_lane, n);
-      hc_s[n] = readlane(hc_lane, n);
+    for (int j = 0; j < kOwnN; ++j) {
+      a2_s[j] = readlane(a2_lane, own_state(j));
+      hc_s[j] = readlane(hc_lane, own_state(j));
     }
   }
 
@@ -289,8 +292,8 @@ scan_fwd_kernel(KParams p) {
       if (n < N) {
         float a2, hc;
         if constexpr (kN != 0) {
-          a2 = a2_s[n];
-          hc = hc_s[n];
+          a2 = a2_s[g * G + nl];
+          hc = hc_s[g * G + nl];
         } else {
           a2 = readlane(a2_lane, n);
           hc = readlane(hc_lane, n);
@@ -322,7 +325,7 @@ scan_fwd_kernel(KParams p) {
         wave_scan_inclusive(aseg, bseg);  // bseg: state at the end of this lane's steps
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
         if constexpr (kN != 0)  // carry into the next chunk
-          hc_s[n] = readlane(bseg, 63);
+          hc_s[g * G + nl] = readlane(bseg, 63);
         else
           hc_lane = writelane(hc_lane, readlane(bseg, 63), n);
         if constexpr (kCkpt) {
@@ -363,7 +366,7 @@ scan_fwd_kernel(KParams p) {
     sdt = 0.0f;
     if constexpr (kCkpt && kN != 0) {  // the carries, one per lane again, for that store
 #pragma unroll
-      for (int n = 0; n < kN; ++n) hc_lane = writelane(hc_lane, hc_s[n], n);
+      for (int j = 0; j < kOwnN; ++j) hc_lane = writelane(hc_lane, hc_s[j], own_state(j));
     }
     if (kCkpt && active && lane < N && own)  // the state entering the chunk
       ck_buf.store4(__float_as_uint(hc_lane), uint32_t(kCkptPerChunk * c * N + lane) * 4u);
@@ -493,7 +496,7 @@ scan_fwd_kernel(KParams p) {
 
   if constexpr (kN != 0) {
 #pragma unroll
-    for (int n = 0; n < kN; ++n) hc_lane = writelane(hc_lane, hc_s[n], n);
+    for (int j = 0; j < kOwnN; ++j) hc_lane = writelane(hc_lane, hc_s[j], own_state(j));
   }
   if (active && p.final_state && lane < N && own) p.final_state[row * N + lane] = hc_lane;
 }
@@ -543,6 +546,22 @@ bool fp32_split(int64_t workgroups, int waves_per_channel) {
   return cus > 0 && workgroups <= cus;
 }
 
+template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kCkpt, bool kMask,
+          int S>
+void launch_form(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
+  // 16 states on aligned rows without a mask: the form with the state count fixed (the same
+  // arithmetic, bit for bit, as the general one).
+  if constexpr (kVecRows && !kMask) {
+    if (p.dstate == 16) {
+      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, kCkpt, kMask, S, 16>),
+                         grid, block, 0, s, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, kCkpt, kMask, S>), grid,
+                     block, 0, s, p);
+}
+
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kMask>
 void launch_flavour(bool ckpt, bool split, dim3 grid, dim3 block, hipStream_t s,
                     const KParams& p) {
@@ -552,32 +571,14 @@ void launch_flavour(bool ckpt, bool split, dim3 grid, dim3 block, hipStream_t s,
     if constexpr (sizeof(Elem) == 4) {
       const dim3 block2(block.x * 2);
       if (ckpt)
-        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask, 2>), grid,
-                           block2, 0, s, p);
+        launch_form<Elem, T, K, G, kVecRows, kDma, true, kMask, 2>(grid, block2, s, p);
       else
-        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask, 2>), grid,
-                           block2, 0, s, p);
+        launch_form<Elem, T, K, G, kVecRows, kDma, false, kMask, 2>(grid, block2, s, p);
     }
   } else if (ckpt) {
-    if constexpr (sizeof(Elem) == 2 && kVecRows && !kMask) {
-      if (p.dstate == 16) {
-        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask, 1, 16>),
-                           grid, block, 0, s, p);
-        return;
-      }
-    }
-    hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, true, kMask>), grid, block,
-                       0, s, p);
+    launch_form<Elem, T, K, G, kVecRows, kDma, true, kMask, 1>(grid, block, s, p);
   } else {
-    if constexpr (sizeof(Elem) == 2 && kVecRows && !kMask) {
-      if (p.dstate == 16) {  // 16 states: the unrolled form (the same arithmetic, bit for bit)
-        hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask, 1, 16>),
-                           grid, block, 0, s, p);
-        return;
-      }
-    }
-    hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, false, kMask>), grid,
-                       block, 0, s, p);
+    launch_form<Elem, T, K, G, kVecRows, kDma, false, kMask, 1>(grid, block, s, p);
   }
 }
 
