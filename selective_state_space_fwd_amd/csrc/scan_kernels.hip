@@ -549,9 +549,9 @@ bool fp32_split(int64_t workgroups, int waves_per_channel) {
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kCkpt, bool kMask,
           int S>
 void launch_form(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
-  // 16 states on aligned rows without a mask: the form with the state count fixed (the same
-  // arithmetic, bit for bit, as the general one).
-  if constexpr (kVecRows && !kMask) {
+  // 16 states on aligned rows: the form with the state count fixed (the same arithmetic, bit
+  // for bit, as the general one).
+  if constexpr (kVecRows) {
     if (p.dstate == 16) {
       hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, kCkpt, kMask, S, 16>),
                          grid, block, 0, s, p);
