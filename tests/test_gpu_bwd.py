@@ -138,8 +138,9 @@ def test_backward_optional_inputs(variant, io):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_saved_states_and_forward_unchanged(io):
-    w = WORKLOADS["tiny"].with_(batch=2, dim=6, dstate=16, seqlen=1700, io=io, gate=True,
+@pytest.mark.parametrize("seqlen", [1700, 2048])  # bf16 rows: element-wise, then whole words
+def test_saved_states_and_forward_unchanged(io, seqlen):
+    w = WORKLOADS["tiny"].with_(batch=2, dim=6, dstate=16, seqlen=seqlen, io=io, gate=True,
                                 initial_state=True, seed=63)
     announce(w.describe() + " saved states")
     inp, dout, dfin = setup(w, seed=63)
