@@ -98,7 +98,7 @@ __device__ __forceinline__ void set_priority_by_work_left(int left, int total) {
 // hands its share of y to the first through LDS; for launches with too few channels to give
 // every SIMD two waves. Each wave carries, and saves, the states it scans.
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDmaInputs, bool kCkpt,
-          bool kMask, int S = 1, int kN = 0>
+          bool kMask, int S = 1, int kN = 0, bool kLate = false>
 // The bf16 saved-state forms and the unrolled fixed-state form are held to four waves per
 // SIMD (128 VGPRs): unbounded, the saved-state store's per-lane offset, or the unrolled
 // schedule, takes them two registers past it.
@@ -125,6 +125,11 @@ scan_fwd_kernel(KParams p) {
   static_assert(!kDmaInputs || kVecRows, "input DMA moves whole aligned 16-byte words");
   static_assert(S == 1 || S == 2, "one or two waves per channel");
   static_assert(kN == 0 || (kN % (G * S) == 0 && kN <= 64), "a fixed state count: whole groups");
+  // kLate: the next chunk's u and delta are loaded after the current chunk's state groups,
+  // ahead of its gate and stores, rather than at its first group: the prefetch registers
+  // (fp32: 32) are then live only through the chunk's tail, which leaves room for a third
+  // wave per SIMD.
+  static_assert(!kLate || !kDmaInputs, "late loads are register loads");
 
   // Staging: [buffer][B=0 / C=1][state-in-group][quad][lane] as float4 (fp32 slots).
   __shared__ float4 lds_bc[2][2][kGS * kQuads * 64];
@@ -432,7 +437,7 @@ scan_fwd_kernel(KParams p) {
         // registers; fetch the next chunk's. Loads complete in order, so the first wait
         // that covers them is the commit of the next group.
         if constexpr (kDmaInputs) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        load_inputs(c + 1);
+        if constexpr (!kLate) load_inputs(c + 1);
         asm volatile("" ::: "memory");  // the DMA stays ahead of the z loads below
       }
       if (g == n_groups - 1 && half == 0) load_z(c);
@@ -459,6 +464,7 @@ scan_fwd_kernel(KParams p) {
       for (int g = 0; g < n_groups; ++g) group_step(g);
     }
 
+    if constexpr (kLate) load_inputs(c + 1);
     if constexpr (S == 2) {
       // The second wave's share of y joins the first's; the first then gates and stores.
       // lds_y is written again only at the end of the next chunk, after at least one more
@@ -546,43 +552,57 @@ bool fp32_split(int64_t workgroups, int waves_per_channel) {
   return cus > 0 && workgroups <= cus;
 }
 
+// fp32 channels too many for the two-wave form in four-channel workgroups to run in one round
+// (more workgroups than compute units), but few enough for six-channel ones: those take the
+// two-wave form with six channels per workgroup and late input loads, at most 168 VGPRs,
+// i.e. one 12-wave workgroup (three waves per SIMD) per compute unit, one round. Aligned
+// rows only, and not when the caller fixes the waves per channel.
+bool fp32_wide_split(const FwdArgs& a) {
+  if (a.waves_per_channel != 0 || !a.vec_ok) return false;
+  const int cus = device_cus();
+  const int64_t four = a.batch * ((a.dim + 3) / 4), six = a.batch * ((a.dim + 5) / 6);
+  return cus > 0 && four > cus && six <= cus;
+}
+
 template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kCkpt, bool kMask,
-          int S>
+          int S, bool kLate>
 void launch_form(dim3 grid, dim3 block, hipStream_t s, const KParams& p) {
   // 16 states on aligned rows: the form with the state count fixed (the same arithmetic, bit
   // for bit, as the general one).
   if constexpr (kVecRows) {
     if (p.dstate == 16) {
-      hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, kCkpt, kMask, S, 16>),
-                         grid, block, 0, s, p);
+      hipLaunchKernelGGL(
+          (scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, kCkpt, kMask, S, 16, kLate>), grid,
+          block, 0, s, p);
       return;
     }
   }
-  hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, kCkpt, kMask, S>), grid,
-                     block, 0, s, p);
+  hipLaunchKernelGGL((scan_fwd_kernel<Elem, T, K, G, kVecRows, kDma, kCkpt, kMask, S, 0, kLate>),
+                     grid, block, 0, s, p);
 }
 
-template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kMask>
+template <typename Elem, int T, int K, int G, bool kVecRows, bool kDma, bool kMask, bool kLate>
 void launch_flavour(bool ckpt, bool split, dim3 grid, dim3 block, hipStream_t s,
                     const KParams& p) {
   // The training forward takes the same form as the plain one, so that both write the same
-  // output bit for bit.
-  if (sizeof(Elem) == 4 && split) {
+  // output bit for bit. The late-load shape exists only as the two-wave form.
+  if ((sizeof(Elem) == 4 && split) || kLate) {
     if constexpr (sizeof(Elem) == 4) {
       const dim3 block2(block.x * 2);
       if (ckpt)
-        launch_form<Elem, T, K, G, kVecRows, kDma, true, kMask, 2>(grid, block2, s, p);
+        launch_form<Elem, T, K, G, kVecRows, kDma, true, kMask, 2, kLate>(grid, block2, s, p);
       else
-        launch_form<Elem, T, K, G, kVecRows, kDma, false, kMask, 2>(grid, block2, s, p);
+        launch_form<Elem, T, K, G, kVecRows, kDma, false, kMask, 2, kLate>(grid, block2, s, p);
     }
-  } else if (ckpt) {
-    launch_form<Elem, T, K, G, kVecRows, kDma, true, kMask, 1>(grid, block, s, p);
-  } else {
-    launch_form<Elem, T, K, G, kVecRows, kDma, false, kMask, 1>(grid, block, s, p);
+  } else if constexpr (!kLate) {
+    if (ckpt)
+      launch_form<Elem, T, K, G, kVecRows, kDma, true, kMask, 1, false>(grid, block, s, p);
+    else
+      launch_form<Elem, T, K, G, kVecRows, kDma, false, kMask, 1, false>(grid, block, s, p);
   }
 }
 
-template <typename Elem, int T, int K, int G, bool kDma>
+template <typename Elem, int T, int K, int G, bool kDma, bool kLate = false>
 int launch_typed(const FwdArgs& a, hipStream_t s) {
   KParams p;
   p.u = a.u;
@@ -610,14 +630,14 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
   const bool split = sizeof(Elem) == 4 && fp32_split(blocks, a.waves_per_channel);
   if (a.vec_ok) {
     if (a.mask)
-      launch_flavour<Elem, T, K, G, true, kDma, true>(ck, split, grid, block, s, p);
+      launch_flavour<Elem, T, K, G, true, kDma, true, kLate>(ck, split, grid, block, s, p);
     else
-      launch_flavour<Elem, T, K, G, true, kDma, false>(ck, split, grid, block, s, p);
-  } else {
+      launch_flavour<Elem, T, K, G, true, kDma, false, kLate>(ck, split, grid, block, s, p);
+  } else if constexpr (!kLate) {
     if (a.mask)
-      launch_flavour<Elem, T, K, G, false, false, true>(ck, split, grid, block, s, p);
+      launch_flavour<Elem, T, K, G, false, false, true, false>(ck, split, grid, block, s, p);
     else
-      launch_flavour<Elem, T, K, G, false, false, false>(ck, split, grid, block, s, p);
+      launch_flavour<Elem, T, K, G, false, false, false, false>(ck, split, grid, block, s, p);
   }
   return int(hipGetLastError());
 }
@@ -657,6 +677,7 @@ int launch_scan_fwd(const FwdArgs& a, void* stream) {
 int launch_scan_chunked(const FwdArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.io == Io::BF16) return launch_typed<uint16_t, SSM_BF16_T, SSM_BF16_K, SSM_BF16_G, SSM_BF16_DMA>(a, s);
+  if (fp32_wide_split(a)) return launch_typed<float, SSM_F32_T, 6, SSM_F32_G, false, true>(a, s);
   return launch_typed<float, SSM_F32_T, SSM_F32_K, SSM_F32_G, SSM_F32_DMA>(a, s);
 }
 

@@ -130,3 +130,28 @@ def test_automatic_choice_matches_a_forced_form():
     auto = run_hip(inp)
     forced = [run_hip(inp, waves_per_channel=k) for k in FORMS]
     assert any(np.array_equal(auto[0], f[0]) and np.array_equal(auto[1], f[1]) for f in forced)
+
+
+@pytest.mark.parametrize("n", [16, 8, 17])
+def test_six_channel_two_wave_shape(n):
+    """1 100 channels: too many for the two-wave form in four-channel workgroups to run in
+    one round on a 256-CU device, few enough in six-channel ones, which the library then
+    takes (late input loads, three waves per SIMD). The per-channel arithmetic is that of the
+    two-wave form, so out and the final state are bitwise those of the forced two-wave
+    launch (four-channel workgroups); both against the oracle; the training forward writes
+    the same out bit for bit."""
+    w = WORKLOADS["tiny"].with_(batch=1, dim=1100, dstate=n, seqlen=1100, io="f32", gate=True,
+                                initial_state=True, a_kind="scaled" if n != 16 else "s4d",
+                                seed=970 + n)
+    announce(f"{w.describe()} six-channel two-wave shape")
+    inp = make_inputs(w)
+    auto = run_hip(inp)
+    two = run_hip(inp, waves_per_channel=2)
+    assert np.array_equal(auto[0], two[0]) and np.array_equal(auto[1], two[1])
+    _check(auto[0], auto[1], _oracle(inp), f"{w.describe()} automatic")
+    t = torch()
+    g = {k: dev(inp[k], "f32") for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")}
+    out, fin, _ = ssm.scan_train(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                                 delta_bias=g["delta_bias"], delta_softplus=True, h0=g["h0"])
+    t.cuda.synchronize()
+    assert np.array_equal(host(out), auto[0]) and np.array_equal(host(fin), auto[1])
