@@ -137,6 +137,10 @@ scan_fwd_kernel(KParams p) {
   __shared__ uint4 lds_in[kDmaInputs ? K * S : 1][2][kBlocks][64];
   // S = 2: the second wave's share of y at the end of a chunk, [channel][quad][lane].
   __shared__ float4 lds_y[S == 2 ? K : 1][S == 2 ? kQuads : 1][64];
+  // Late-load two-wave form: each wave of a channel forms the step sizes and dt u of half of
+  // every lane's steps and takes the other half from its partner here:
+  // [channel][dt / du][quad][lane].
+  __shared__ float4 lds_steps[kLate ? K : 1][2][kLate ? kQuads : 1][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,7 +248,12 @@ scan_fwd_kernel(KParams p) {
   // ---- inputs of a chunk. With DMA, u and delta land in this wave's LDS words; z is
   // loaded into registers at the start of the chunk's last group. Past the last chunk the
   // offsets fall outside the row and read zeros.
-  uint4 nu[kDmaInputs ? 1 : kBlocks], nd[kDmaInputs ? 1 : kBlocks], zraw[kBlocks];
+  // In the late-load two-wave form each wave loads the u and delta of its own half of the
+  // lane's steps (blocks [half kOwnBlocks, (half + 1) kOwnBlocks)); otherwise all of them.
+  constexpr int kOwnBlocks = kLate ? kBlocks / 2 : kBlocks;
+  static_assert(!kLate || (S == 2 && kBlocks % 2 == 0 && !kDmaInputs),
+                "late loads: two waves, register loads, even halves");
+  uint4 nu[kDmaInputs ? 1 : kOwnBlocks], nd[kDmaInputs ? 1 : kOwnBlocks], zraw[kBlocks];
   auto load_inputs = [&](int c) {
     const uint32_t tb = uint32_t(c) * kChunk + uint32_t(lane) * T;
     if constexpr (kDmaInputs) {
@@ -256,10 +265,11 @@ scan_fwd_kernel(KParams p) {
                                                  (tb + q * kVec) * kEsz, 0, 0, 0);
       }
     } else {
+      const uint32_t ob = kLate ? uint32_t(half * kOwnBlocks * kVec) : 0u;  // uniform
 #pragma unroll
-      for (int q = 0; q < kBlocks; ++q) {
-        nu[q] = load_word<Elem, kVecRows>(u_buf, tb + q * kVec);
-        nd[q] = load_word<Elem, kVecRows>(dl_buf, tb + q * kVec);
+      for (int q = 0; q < kOwnBlocks; ++q) {
+        nu[q] = load_word<Elem, kVecRows>(u_buf, tb + ob + q * kVec);
+        nd[q] = load_word<Elem, kVecRows>(dl_buf, tb + ob + q * kVec);
       }
     }
   };
@@ -380,48 +390,122 @@ scan_fwd_kernel(KParams p) {
                             : 0x80000000u;
     {
       const bool tail = (c + 1) * kChunk > L;
-#pragma unroll
-      for (int q = 0; q < kBlocks; ++q) {
-        uint4 wu, wd;
-        if constexpr (kDmaInputs) {
-          wu = lds_in[wave][0][q][lane];
-          wd = lds_in[wave][1][q][lane];
-        } else {
-          wu = nu[q];
-          wd = nd[q];
-        }
-        float uv[kVec], dr[kVec];
-        widen_raw16<Elem>(wu, uv);
-        widen_raw16<Elem>(wd, dr);
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          const int j = q * kVec + e;
-          dt[j] = dr[e] + bias_d;
-          du[j] = uv[e];  // u for now; times the step size below
-          y[j] = half == 0 ? Dd * uv[e] : 0.0f;  // the D skip once per channel
-        }
-      }
       // Each flag is tested once per chunk, around whole loops: a test per step would be
       // turned into a select per step, paid on every chunk.
-      if (p.softplus) {
+      if constexpr (!kLate) {
 #pragma unroll
-        for (int j = 0; j < T; ++j) dt[j] = softplus_f(dt[j]);
-      }
-      if (tail) {  // steps past L: identity (dA = 1, dBu = 0)
+        for (int q = 0; q < kBlocks; ++q) {
+          uint4 wu, wd;
+          if constexpr (kDmaInputs) {
+            wu = lds_in[wave][0][q][lane];
+            wd = lds_in[wave][1][q][lane];
+          } else {
+            wu = nu[q];
+            wd = nd[q];
+          }
+          float uv[kVec], dr[kVec];
+          widen_raw16<Elem>(wu, uv);
+          widen_raw16<Elem>(wd, dr);
 #pragma unroll
-        for (int j = 0; j < T; ++j) dt[j] = (tb + j < L) ? dt[j] : 0.0f;
-      }
+          for (int e = 0; e < kVec; ++e) {
+            const int j = q * kVec + e;
+            dt[j] = dr[e] + bias_d;
+            du[j] = uv[e];  // u for now; times the step size below
+            y[j] = half == 0 ? Dd * uv[e] : 0.0f;  // the D skip once per channel
+          }
+        }
+        if (p.softplus) {
 #pragma unroll
-      for (int j = 0; j < T; ++j) du[j] *= dt[j];
-      if constexpr (kMask) {
-        // A padding step keeps the state: a zero step size makes it the identity (dA = 1,
-        // dBu = 0) while y still reads the state.
-        const uint8_t* m = p.mask + int64_t(b) * L;
+          for (int j = 0; j < T; ++j) dt[j] = softplus_f(dt[j]);
+        }
+        if (tail) {  // steps past L: identity (dA = 1, dBu = 0)
 #pragma unroll
-        for (int j = 0; j < T; ++j) {
-          const bool live = (tb + j < L) && m[tb + j] != 0;
-          dt[j] = live ? dt[j] : 0.0f;
-          du[j] = live ? du[j] : 0.0f;
+          for (int j = 0; j < T; ++j) dt[j] = (tb + j < L) ? dt[j] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < T; ++j) du[j] *= dt[j];
+        if constexpr (kMask) {
+          // A padding step keeps the state: a zero step size makes it the identity (dA = 1,
+          // dBu = 0) while y still reads the state.
+          const uint8_t* m = p.mask + int64_t(b) * L;
+#pragma unroll
+          for (int j = 0; j < T; ++j) {
+            const bool live = (tb + j < L) && m[tb + j] != 0;
+            dt[j] = live ? dt[j] : 0.0f;
+            du[j] = live ? du[j] : 0.0f;
+          }
+        }
+      } else {
+        // Late-load two-wave form: each wave forms the step sizes and dt u of its own half
+        // of the lane's steps (lo = half T / 2 on), the same way, writes them to LDS and,
+        // after a barrier, reads all T back in order. The D skip goes into the y share of
+        // the wave that owns the step (the two shares are summed at the chunk's end).
+        constexpr int kH = T / 2;
+        const int lo = half * kH;
+        const float d_first = half == 0 ? Dd : 0.0f, d_second = half == 0 ? 0.0f : Dd;
+        float odt[kH], odu[kH];
+#pragma unroll
+        for (int q = 0; q < kOwnBlocks; ++q) {
+          float uv[kVec], dr[kVec];
+          widen_raw16<Elem>(nu[q], uv);
+          widen_raw16<Elem>(nd[q], dr);
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const int k = q * kVec + e;
+            odt[k] = dr[e] + bias_d;
+            odu[k] = uv[e];
+            y[k] = d_first * uv[e];
+            y[kH + k] = d_second * uv[e];
+          }
+        }
+        if (p.softplus) {
+#pragma unroll
+          for (int k = 0; k < kH; ++k) odt[k] = softplus_f(odt[k]);
+        }
+        if (tail) {
+#pragma unroll
+          for (int k = 0; k < kH; ++k) odt[k] = (tb + lo + k < L) ? odt[k] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kH; ++k) odu[k] *= odt[k];
+        if constexpr (kMask) {
+          const uint8_t* m = p.mask + int64_t(b) * L;
+#pragma unroll
+          for (int k = 0; k < kH; ++k) {
+            const bool live = (tb + lo + k < L) && m[tb + lo + k] != 0;
+            odt[k] = live ? odt[k] : 0.0f;
+            odu[k] = live ? odu[k] : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kH / 4; ++q) {
+          lds_steps[slot][0][lo / 4 + q][lane] =
+              make_float4(odt[4 * q], odt[4 * q + 1], odt[4 * q + 2], odt[4 * q + 3]);
+          lds_steps[slot][1][lo / 4 + q][lane] =
+              make_float4(odu[4 * q], odu[4 * q + 1], odu[4 * q + 2], odu[4 * q + 3]);
+        }
+        __syncthreads();
+        const int po = kH - lo;  // the partner's first step
+        float pdt[kH], pdu[kH];
+#pragma unroll
+        for (int q = 0; q < kH / 4; ++q) {
+          const float4 a = lds_steps[slot][0][po / 4 + q][lane];
+          const float4 u4 = lds_steps[slot][1][po / 4 + q][lane];
+          pdt[4 * q] = a.x;
+          pdt[4 * q + 1] = a.y;
+          pdt[4 * q + 2] = a.z;
+          pdt[4 * q + 3] = a.w;
+          pdu[4 * q] = u4.x;
+          pdu[4 * q + 1] = u4.y;
+          pdu[4 * q + 2] = u4.z;
+          pdu[4 * q + 3] = u4.w;
+        }
+#pragma unroll
+        for (int k = 0; k < kH; ++k) {
+          dt[k] = half == 0 ? odt[k] : pdt[k];
+          du[k] = half == 0 ? odu[k] : pdu[k];
+          dt[kH + k] = half == 0 ? pdt[k] : odt[k];
+          du[kH + k] = half == 0 ? pdu[k] : odu[k];
         }
       }
 #pragma unroll

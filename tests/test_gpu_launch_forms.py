@@ -136,10 +136,11 @@ def test_automatic_choice_matches_a_forced_form():
 def test_six_channel_two_wave_shape(n):
     """1 100 channels: too many for the two-wave form in four-channel workgroups to run in
     one round on a 256-CU device, few enough in six-channel ones, which the library then
-    takes (late input loads, three waves per SIMD). The per-channel arithmetic is that of the
-    two-wave form, so out and the final state are bitwise those of the forced two-wave
-    launch (four-channel workgroups); both against the oracle; the training forward writes
-    the same out bit for bit."""
+    takes (late input loads, three waves per SIMD, each wave forming the step sizes of half
+    of a lane's steps). The states are scanned as in the forced two-wave launch (four-channel
+    workgroups), so the final state is bitwise that launch's; the D skip joins y in the other
+    wave's share for half of the steps, so out agrees to float32 rounding; both against the
+    oracle; the training forward writes the same out bit for bit."""
     w = WORKLOADS["tiny"].with_(batch=1, dim=1100, dstate=n, seqlen=1100, io="f32", gate=True,
                                 initial_state=True, a_kind="scaled" if n != 16 else "s4d",
                                 seed=970 + n)
@@ -147,7 +148,8 @@ def test_six_channel_two_wave_shape(n):
     inp = make_inputs(w)
     auto = run_hip(inp)
     two = run_hip(inp, waves_per_channel=2)
-    assert np.array_equal(auto[0], two[0]) and np.array_equal(auto[1], two[1])
+    assert np.array_equal(auto[1], two[1]), "final states differ from the forced two-wave launch"
+    np.testing.assert_allclose(auto[0], two[0], rtol=1e-5, atol=1e-5 * float(np.abs(two[0]).max()))
     _check(auto[0], auto[1], _oracle(inp), f"{w.describe()} automatic")
     t = torch()
     g = {k: dev(inp[k], "f32") for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias", "h0")}
