@@ -49,7 +49,7 @@ FLOPS_PER_UPDATE = 6
 EXPS_PER_UPDATE = 1
 EXP_PEAK_PER_S = ALU_PEAK_TFLOPS * 1e12 / 2 / 4
 # The 157.3 TFLOP/s figure needs packed fp32 (v_pk_fma_f32: two fp32 FMAs per lane per
-# instruction), which this build disables. Without it a SIMD retires 16 fp32 FMA lanes per
+# instruction), which the library is compiled without. Without it a SIMD retires 16 fp32 FMA lanes per
 # clock: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz = 78.6 TFLOP/s, a wave64 v_fma_f32
 # every 4 clocks and a wave64 v_exp_f32 every 8 (bench.py --alu-probe measures both). The
 # same update then costs 4 issue slots plus 2 for the exp: 12 flop-equivalents at 78.6.
@@ -226,7 +226,7 @@ def copy_probe(torch, steps: int, warmup: int) -> int:
 
 
 def alu_probe(torch, steps: int, warmup: int) -> int:
-    """VALU issue rates under this build's flags: independent chains of wave64 v_fma_f32 and
+    """VALU issue rates under the library's compile flags: independent chains of wave64 v_fma_f32 and
     of wave64 v_exp_f32 (libssmprobe.so), at 16 waves per CU. Prints one JSON line."""
     import ctypes
 
