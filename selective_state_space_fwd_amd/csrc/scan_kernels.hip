@@ -19,8 +19,9 @@
 //     buffered: the global loads of the next group are in flight while the current group
 //     is computed (the tiling / double-buffering idea of ybb.press sections 3.3 and 4.3,
 //     with parameters kept on chip). The LDS layout is lane-interleaved: for a fixed state
-//     and quad of steps, the 64 lanes read 64 consecutive 16-byte words, so each
-//     ds_read_b128 is bank-conflict free.
+//     and quad of steps, the 64 lanes read 64 consecutive 16-byte words (in fp32 stages
+//     permuted within groups of eight, so that the stage's writes are conflict free too),
+//     so each ds_read_b128 is bank-conflict free.
 //   * Per state n (diagonal A: the N chains are independent, mhpq.cn/news/1057127
 //     section 1):
 //       1. discretise the lane's T steps: dA = exp2(dt * A*log2 e), dBu = (dt*u) * B;
@@ -192,6 +193,15 @@ scan_fwd_kernel(KParams p) {
   const int n_groups = (N + kGS - 1) / kGS;
   const int n_chunks = (L + kChunk - 1) / kChunk;
 
+  // fp32 stages are written one 16-byte word per thread, consecutive threads on consecutive
+  // quads of one lane's steps: unswizzled, the four quads of a lane sit 1 KB apart, on the
+  // same banks, and every write instruction conflicts four ways. Lane l's word of quad q goes
+  // to slot l ^ 2q of the quad's row instead: a write instruction's eight lanes per LDS pass
+  // then fill all 32 banks, and a read of one quad by 64 lanes stays a permutation of
+  // consecutive slots within each group of eight. (bf16 stages are written as 16-bit halves
+  // in another order, and keep the plain layout.)
+  auto swz = [](int q, int l) { return kBf16 ? l : (l ^ (2 * q)); };
+
   // ---- B/C staging. Word w of a stage: array w / kArrayWords, state-in-group
   // (w % kArrayWords) / kWordsPerState, steps [s, s + kVec) with
   // s = (w % kWordsPerState) * kVec; in LDS at lane s / T, quad (s % T) / 4.
@@ -204,7 +214,7 @@ scan_fwd_kernel(KParams p) {
     st_a[k] = __builtin_amdgcn_readfirstlane(w / kArrayWords);
     st_nl[k] = (w < kStageWords) ? wa / kWordsPerState : kGS;  // kGS: this lane holds no word
     st_s[k] = (wa % kWordsPerState) * kVec;
-    st_idx[k] = (st_nl[k] * kQuads + (st_s[k] % T) / 4) * 64 + st_s[k] / T;
+    st_idx[k] = (st_nl[k] * kQuads + (st_s[k] % T) / 4) * 64 + swz((st_s[k] % T) / 4, st_s[k] / T);
   }
   uint4 raw[kWordsPerLane];
   // Stage `it` (chunk it / n_groups, group it % n_groups); past the end it reads zeros.
@@ -313,13 +323,13 @@ scan_fwd_kernel(KParams p) {
           a2 = readlane(a2_lane, n);
           hc = readlane(hc_lane, n);
         }
-        const float4* Bq = &lds_bc[buf][0][sl * kQuads * 64 + lane];
-        const float4* Cq = &lds_bc[buf][1][sl * kQuads * 64 + lane];
+        const float4* Bq = &lds_bc[buf][0][sl * kQuads * 64];
+        const float4* Cq = &lds_bc[buf][1][sl * kQuads * 64];
         // All of this state's B words are requested at once, and its C words before the
         // wave scan, so LDS latency overlaps the exps and the scan.
         float4 bq[kQuads], cq[kQuads];
 #pragma unroll
-        for (int q = 0; q < kQuads; ++q) bq[q] = Bq[q * 64];
+        for (int q = 0; q < kQuads; ++q) bq[q] = Bq[q * 64 + swz(q, lane)];
         float dA[T], dBu[T];
 #pragma unroll
         for (int j = 0; j < T; ++j) dA[j] = exp2_hw(dt[j] * a2);
@@ -335,7 +345,7 @@ scan_fwd_kernel(KParams p) {
           }
         }
 #pragma unroll
-        for (int q = 0; q < kQuads; ++q) cq[q] = Cq[q * 64];
+        for (int q = 0; q < kQuads; ++q) cq[q] = Cq[q * 64 + swz(q, lane)];
         float aseg = exp2_hw(sdt * a2);
         wave_scan_inclusive(aseg, bseg);  // bseg: state at the end of this lane's steps
         float h = shift_up_one(bseg, hc);  // state entering this lane's steps
