@@ -78,6 +78,14 @@ extern "C" {
  * order (outputs equal to fp32 rounding). Sequences of at most 32 steps ignore the hint. */
 #define SSM_WAVES_PER_CHANNEL_1 (1u << 8)
 #define SSM_WAVES_PER_CHANNEL_2 (1u << 9)
+/* Backward (ssm_scan_bwd and ssm_scan_bwd_workspace_bytes) only: keep every channel's whole
+ * sequence in one workgroup. Without it, a backward with a workspace on a problem whose
+ * channels alone do not fill the device cuts each sequence into segments of whole saved-state
+ * intervals, scanned by different workgroups from the state adjoint carried into them (a
+ * first launch finds each segment's adjoint from a zero start; the carries are then combined
+ * right to left, which p1 section 3.3's chunked backward implies). The two forms agree to fp32
+ * rounding; each is bitwise reproducible. */
+#define SSM_BWD_UNSPLIT (1u << 10)
 
 /* status codes */
 #define SSM_OK 0
@@ -204,8 +212,12 @@ SSM_API int ssm_scan_bwd(const void* u, const void* delta, const float* A, const
 /*
  * Bytes of workspace ssm_scan_bwd needs for reproducible sums: each workgroup's sums of dB
  * and dC over its channels (32 channels per workgroup, whatever the storage type in flags
- * bits 0-1), 2 x dstate x seqlen fp32 per workgroup, and dA, dD and dbias per batch row. 0 for empty problems; -1 for negative sizes, an unknown storage
- * type or a size past int64.
+ * bits 0-1), 2 x dstate x seqlen fp32 per workgroup, and dA, dD and dbias per batch row and
+ * segment, plus each segment's carried adjoint when the current device's rule cuts the
+ * sequences into segments (see SSM_BWD_UNSPLIT; the size then depends on the device's
+ * compute-unit count). ssm_scan_bwd uses as many segments as the workspace it is given holds,
+ * down to none: a workspace of the size queried with SSM_BWD_UNSPLIT always works. 0 for
+ * empty problems; -1 for negative sizes, an unknown storage type or a size past int64.
  */
 SSM_API int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate,
                                              int64_t seqlen, uint32_t flags);

@@ -33,6 +33,7 @@ SSM_DELTA_SOFTPLUS = 1 << 4
 SSM_INITIAL_STATE = 1 << 5
 SSM_WAVES_PER_CHANNEL_1 = 1 << 8
 SSM_WAVES_PER_CHANNEL_2 = 1 << 9
+SSM_BWD_UNSPLIT = 1 << 10
 
 SSM_OK = 0
 SSM_ERR_INVALID_ARG = -1
@@ -327,7 +328,7 @@ def scan_train(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplu
 
 def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_bias=None,
                   delta_softplus: bool = False, dfinal=None, want_dh0: bool = True, mask=None,
-                  deterministic: bool = True, workspace=None
+                  deterministic: bool = True, workspace=None, unsplit: bool = False
                   ) -> Dict[str, Optional["torch.Tensor"]]:
     """Gradients of sum(dout * out) + sum(dfinal * final_state) for the forward on the same
     inputs. Returns du, ddelta, dz (u's dtype), dA, dB, dC, dD, dbias, dh0 (float32; None
@@ -336,7 +337,8 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
     deterministic: sum dA, dB, dC, dD and dbias through a workspace in a fixed order
     (bitwise reproducible; ssm_scan_bwd_workspace_bytes of device memory, allocated here
     unless ``workspace``, a uint8 device tensor at least that large, is given); False: float
-    atomics, no workspace."""
+    atomics, no workspace. unsplit: SSM_BWD_UNSPLIT (each channel's whole sequence in one
+    workgroup, no segments)."""
     import torch
 
     u, delta, A, B, C, D, z, delta_bias, mask, chunk_states, dout, dfinal = _dense(
@@ -357,6 +359,8 @@ def scan_backward(u, delta, A, B, C, chunk_states, dout, D=None, z=None, delta_b
         raise ValueError("dfinal must be a contiguous float32 [batch, dim, dstate] tensor")
     if delta_softplus:
         flags |= SSM_DELTA_SOFTPLUS
+    if unsplit:
+        flags |= SSM_BWD_UNSPLIT
     dev = u.device
     f32 = dict(device=dev, dtype=torch.float32)
     g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),

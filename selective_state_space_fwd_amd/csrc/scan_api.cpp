@@ -188,16 +188,32 @@ int ssm_scan_fwd_ckpt(const void* u, const void* delta, const float* A, const vo
 
 int64_t ssm_scan_ckpt_count(int64_t seqlen) { return ckpt_count(seqlen); }
 
+namespace {
+
+// Bytes of a backward workspace laid out for `segments` segments (-1 on overflow).
+int64_t bwd_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, ssm::Io io,
+                  int64_t segments) {
+  ssm::BwdWorkspace w;
+  if (!ssm::bwd_workspace(batch, dim, dstate, seqlen, io, segments, &w)) return -1;
+  return w.floats * 4;
+}
+
+// The segments a backward on the current device would cut each sequence into.
+int64_t bwd_segments_here(int64_t batch, int64_t dim, int64_t seqlen, ssm::Io io,
+                          uint32_t flags) {
+  if (flags & SSM_BWD_UNSPLIT) return 1;
+  return ssm::bwd_segments(batch, dim, seqlen, io, ssm::device_cus());
+}
+
+}  // namespace
+
 int64_t ssm_scan_bwd_workspace_bytes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                                      uint32_t flags) {
   if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return -1;
   const uint32_t io = flags & SSM_IO_MASK;
   if (io != SSM_IO_F32 && io != SSM_IO_BF16) return -1;
-  ssm::BwdWorkspace w;
-  if (!ssm::bwd_workspace(batch, dim, dstate, seqlen,
-                          io == SSM_IO_BF16 ? ssm::Io::BF16 : ssm::Io::F32, &w))
-    return -1;
-  return w.floats * 4;
+  const ssm::Io t = io == SSM_IO_BF16 ? ssm::Io::BF16 : ssm::Io::F32;
+  return bwd_bytes(batch, dim, dstate, seqlen, t, bwd_segments_here(batch, dim, seqlen, t, flags));
 }
 
 int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
@@ -207,7 +223,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
                  float* dD, void* dz, float* dbias, float* dh0, void* workspace,
                  int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
                  int64_t seqlen, void* stream) {
-  const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE;
+  const uint32_t known = SSM_IO_MASK | SSM_DELTA_SOFTPLUS | SSM_INITIAL_STATE | SSM_BWD_UNSPLIT;
   if (flags & ~known) return SSM_ERR_INVALID_ARG;
   if (batch < 0 || dim < 0 || dstate < 0 || seqlen < 0) return SSM_ERR_INVALID_ARG;
   const uint32_t io = flags & SSM_IO_MASK;
@@ -243,8 +259,23 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
       !aligned(dC, 4) || (dD && !aligned(dD, 4)) || (dbias && !aligned(dbias, 4)) ||
       (dh0 && !aligned(dh0, 4)) || (workspace && !aligned(workspace, 256)))
     return SSM_ERR_MISALIGNED;
+  // With a workspace: as many segments as this device's rule asks for and the workspace
+  // holds (a workspace of the unsegmented size always works: one segment).
+  const ssm::Io iot = io == SSM_IO_BF16 ? ssm::Io::BF16 : ssm::Io::F32;
+  int64_t segments = 1;
   if (workspace) {
-    const int64_t need = ssm_scan_bwd_workspace_bytes(batch, dim, dstate, seqlen, flags);
+    if (bwd_bytes(batch, dim, dstate, seqlen, iot, 1) < 0) return SSM_ERR_UNSUPPORTED;
+    for (int64_t s = bwd_segments_here(batch, dim, seqlen, iot, flags); s > 1; --s) {
+      const int64_t b = bwd_bytes(batch, dim, dstate, seqlen, iot, s);
+      if (b >= 0 && b <= workspace_bytes) {
+        segments = s;
+        break;
+      }
+    }
+    // the segment count takes whole intervals per segment, none empty
+    const int64_t n = ssm::bwd_intervals(seqlen), per = (n + segments - 1) / segments;
+    segments = per > 0 ? (n + per - 1) / per : 1;
+    const int64_t need = bwd_bytes(batch, dim, dstate, seqlen, iot, segments);
     if (need < 0) return SSM_ERR_UNSUPPORTED;
     if (workspace_bytes < need) return SSM_ERR_INVALID_ARG;
     // The partial sums are written while the inputs are read and read while the summed
@@ -313,6 +344,7 @@ int ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B
   a.dh0 = dh0;
   a.mask = mask;
   a.workspace = static_cast<float*>(workspace);
+  a.segments = workspace ? segments : 1;
   a.batch = batch;
   a.dim = dim;
   a.dstate = dstate;

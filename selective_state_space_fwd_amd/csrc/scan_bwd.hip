@@ -64,6 +64,16 @@ struct BParams {
   // [workgroup][dB, dC][state][step], dC unused; dA at [row][state]; dD and dbias at [row])
   // for bwd_reduce_kernel to add up.
   int partials;
+  // Segments: each channel's sequence cut into nseg runs of seg_chunks intervals (the last
+  // maybe shorter), each its own workgroup; workgroup blockIdx.x takes segment
+  // seg0 + blockIdx.x / wgs of group blockIdx.x % wgs (wgs = batch dblocks). rows = batch
+  // dim: the stride of one segment's slots of dA, dD, dbias and the carries. cq, cp: each
+  // segment's state adjoint from a zero start at its right end, [nseg][rows][dstate], and its
+  // sum of step sizes, [nseg][rows] (written by the carry launch, read by the main one).
+  int nseg, seg0, seg_chunks, wgs;
+  int64_t rows;
+  float* cq;
+  float* cp;
 };
 
 constexpr int kT = 8;                      // steps per lane
@@ -236,8 +246,14 @@ __device__ __forceinline__ void store_steps(const Buf& b, uint32_t e0, int t0, i
 // W: waves per workgroup (2 W channels). M: states between workgroup barriers; the LDS
 // rows of dB and dC have 2 M slots, so that one group of M states is written while the
 // previous one is added up. kMask: read a padding mask (its own instantiation: the unmasked
-// kernel's register count decides how many waves fit on a SIMD).
-template <typename Elem, int W, int M, bool kVecRows, bool kMask>
+// kernel's register count decides how many waves fit on a SIMD). kSeg: a segmented backward
+// (the workgroup takes one segment of its channels' sequences; its own instantiation, so that
+// the whole-sequence kernel's code is not touched). kCarry: the carry launch of a segmented
+// backward: only the state adjoint of each segment from a zero start at its right end (the
+// step sizes, a_t and c_t = C_t dy_t; no recomputed state, no gradient), stored with the
+// segment's sum of step sizes.
+template <typename Elem, int W, int M, bool kVecRows, bool kMask, bool kSeg = false,
+          bool kCarry = false>
 __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   constexpr int kVec = Vec<Elem>::kN;
   constexpr int kSteps = kCkptInterval;  // steps per interval
@@ -263,8 +279,11 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const int hf = lane >> 5;         // which of the wave's two channels
   const int li = lane & 31;         // lane inside the channel
   const bool half_start = li == 0, half_end = li == kHalfLanes - 1;
-  const int b = blockIdx.x / p.dblocks;
-  const int d0 = (blockIdx.x - b * p.dblocks) * (2 * W) + 2 * wave;  // the wave's first channel
+  static_assert(kSeg || !kCarry, "the carry launch belongs to a segmented backward");
+  const int seg = kSeg ? p.seg0 + int(blockIdx.x) / p.wgs : 0;
+  const int wg = kSeg ? int(blockIdx.x) - (seg - p.seg0) * p.wgs : int(blockIdx.x);  // channels
+  const int b = wg / p.dblocks;
+  const int d0 = (wg - b * p.dblocks) * (2 * W) + 2 * wave;  // the wave's first channel
   // Uniform, but the compiler computes the clamp with a vector min/max (v_med3): taken back
   // to a scalar register here, or every buffer descriptor built from it would be treated as
   // divergent (a waterfall loop around each access).
@@ -274,6 +293,10 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const bool active = hf < rows_here;
   const int N = p.dstate, L = p.seqlen;
   const int n_chunks = (L + kSteps - 1) / kSteps;
+  // this segment's intervals, c_lo .. c_hi, processed last to first
+  const int c_lo = kSeg ? seg * p.seg_chunks : 0;
+  const int c_hi =
+      kSeg ? (c_lo + p.seg_chunks < n_chunks ? c_lo + p.seg_chunks : n_chunks) - 1 : n_chunks - 1;
   const int64_t row0 = int64_t(b) * p.dim + (rows_here > 0 ? d0 : 0);
   const int64_t row = row0 + hf;  // this half's channel (meaningful when active)
 
@@ -296,7 +319,16 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const float Dd = (active && p.D) ? p.D[d] : 0.0f;
   const float bias_d = (active && p.bias) ? p.bias[d] : 0.0f;
   for (int n = li; n < N; n += kHalfLanes) {
-    s_adj[wave][hf][n] = (active && p.dfinal) ? p.dfinal[row * N + n] : 0.0f;  // e_{L-1}
+    // e entering from the right: dfinal at the sequence's end (e_L); with segments, what
+    // bwd_carry_kernel combined for this segment. The carry launch starts from zero.
+    float e = 0.0f;
+    if (!kCarry && active) {
+      if (kSeg)
+        e = p.cq[(int64_t(seg) * p.rows + row) * N + n];
+      else
+        e = p.dfinal ? p.dfinal[row * N + n] : 0.0f;
+    }
+    s_adj[wave][hf][n] = e;
     s_dA[wave][hf][n] = 0.0f;
   }
   if (li < 2) s_dDb[wave][hf][li] = 0.0f;
@@ -311,9 +343,9 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   // Where the flush adds this workgroup's dB and dC rows: this batch row of the outputs, or
   // this workgroup's slot of partial sums. Both take the same offset (state, step) after it.
   const int64_t nl = int64_t(N) * L;
-  float* const flush0 = p.partials ? p.dB + int64_t(blockIdx.x) * 2 * nl : p.dB + b * nl;
+  float* const flush0 = p.partials ? p.dB + int64_t(wg) * 2 * nl : p.dB + b * nl;
   float* const flush1 = p.partials ? flush0 + nl : p.dC + b * nl;
-  const int total = n_chunks * N;  // (interval, state) pairs, in processing order
+  const int total = (c_hi - c_lo + 1) * N;  // (interval, state) pairs, in processing order
 
   // The staging words: one 16-byte source word per thread of the first kStageWords. The
   // first M kRowWords threads take B, the next C (a whole number of waves each, so the
@@ -331,13 +363,14 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   auto stage_load = [&](int grp, uint4& st_raw) {  // this thread's word of group grp
     if (st_on) {
       const int i0 = grp * M;  // uniform: the group's first (interval, state) pair
-      int c = n_chunks - 1 - i0 / N, n = i0 - (i0 / N) * N + st_ms;
+      int c = c_hi - i0 / N, n = i0 - (i0 / N) * N + st_ms;
       while (n >= N) {  // the pairs after it take the next states, then the interval before
         n -= N;
         --c;
       }
       const int t = c * kSteps + st_ws;
-      const uint32_t e = (c >= 0 && t < L) ? uint32_t(n) * uint32_t(L) + uint32_t(t) : bc_elems;
+      const uint32_t e =
+          (c >= c_lo && t < L) ? uint32_t(n) * uint32_t(L) + uint32_t(t) : bc_elems;
       st_raw = load_word<Elem, kVecRows>(st_ab == 0 ? B_buf : C_buf, e);
     }
   };
@@ -398,16 +431,17 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const Buf ck_buf(p.ckpt + row0 * p.n_ckpt * N, uint32_t(rows_here * p.n_ckpt * N) * 4u);
   const uint32_t a_off = uint32_t(hf * N) * 4u, ck_off = uint32_t(hf * p.n_ckpt * N) * 4u;
   auto fetch_pair = [&](int c, int n, float& A_out, float& h_out) {
-    if (c < 0) c = n = 0;
+    if (c < c_lo) c = c_lo, n = 0;
     A_out = __uint_as_float(A_buf.load4(a_off, uint32_t(n) * 4u));
     h_out = __uint_as_float(ck_buf.load4(ck_off, uint32_t(c * N + n) * 4u));
   };
   float A_nx, hc_nx;
-  fetch_pair(n_chunks - 1, 0, A_nx, hc_nx);
+  fetch_pair(c_hi, 0, A_nx, hc_nx);
 
   int pair = 0;
-  int grp_c = n_chunks - 1, grp_n = 0;  // the current group's first pair
-  for (int c = n_chunks - 1; c >= 0; --c) {
+  int grp_c = c_hi, grp_n = 0;  // the current group's first pair
+  float seg_sdt = 0.0f;         // the carry launch: this lane's sum of step sizes
+  for (int c = c_hi; c >= c_lo; --c) {
     const int t0 = c * kSteps + li * kT;
     const uint32_t e0 = row_e + uint32_t(t0);
     // Live across the state loop: s, s u, dL/dy, y and the two sums over the states (u
@@ -471,8 +505,9 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       }
       // Formed here: left to the compiler, the sum sinks to its use after the state loop
       // and keeps u live (and spilled) across it.
-      asm volatile("" : "+v"(dD_acc));
+      if constexpr (!kCarry) asm volatile("" : "+v"(dD_acc));
     }
+    if constexpr (kCarry) seg_sdt += sdt;
 
     for (int n = 0; n < N; ++n, ++pair) {
       const float An = A_nx, hc = hc_nx;
@@ -489,21 +524,24 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         const int grp = pair / M;
         if (pair % M == 0) stage_load(grp + 1, st_word);
         const float4* sB = &s_bc[grp & 1][pair % M][0][kT / 4 * li];
+        if constexpr (!kCarry) {
 #pragma unroll
-        for (int q = 0; q < kT / 4; ++q) {
-          const float4 bq = sB[q];
-          Bv[4 * q] = bq.x;
-          Bv[4 * q + 1] = bq.y;
-          Bv[4 * q + 2] = bq.z;
-          Bv[4 * q + 3] = bq.w;
+          for (int q = 0; q < kT / 4; ++q) {
+            const float4 bq = sB[q];
+            Bv[4 * q] = bq.x;
+            Bv[4 * q + 1] = bq.y;
+            Bv[4 * q + 2] = bq.z;
+            Bv[4 * q + 3] = bq.w;
+          }
         }
       }
-      // forward again from the saved state: h_t for this lane's steps
+      // forward again from the saved state: h_t for this lane's steps (the carry launch
+      // needs only the a_t)
       float bseg = half_start ? hc : 0.0f;
 #pragma unroll
       for (int j = 0; j < kT; ++j) {
         dA[j] = exp2_hw(sv[j] * a2);
-        bseg = __builtin_fmaf(dA[j], bseg, su[j] * Bv[j]);
+        if constexpr (!kCarry) bseg = __builtin_fmaf(dA[j], bseg, su[j] * Bv[j]);
       }
       const float alpha = exp2_hw(sdt * a2);  // product of the lane's a_t
       {
@@ -520,13 +558,13 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
           Cv[4 * q + 3] = cq.w;
         }
       }
-      {
+      if constexpr (!kCarry) {
         float aseg = alpha;
         half_scan_inclusive(aseg, bseg);  // bseg: the state after the lane's last step
       }
-      const float up = shift_up_any(bseg);
+      const float up = kCarry ? 0.0f : shift_up_any(bseg);
       const float hin = half_start ? hc : up;  // the state entering the lane's steps
-      {
+      if constexpr (!kCarry) {
         float hh = hin;
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
@@ -551,6 +589,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
                                                                        // to the left
       // dB and dC rows of the step pairs (j, j + 4) are added across the two halves as
       // soon as both exist and go to LDS at once: four steps per lane, 8 li + 4 hf on.
+      if constexpr (!kCarry) {
       float dBr[kT / 2], dCr[kT / 2];
       const int slot = pair % kSlots;
       float* const rowB = reinterpret_cast<float*>(&acc[slot][0][wave][2 * li + hf]);
@@ -577,11 +616,12 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       }
       dAn = half_sum_to_last(dAn);
       if (half_end) atomicAdd(&s_dA[wave][hf][n], dAn);  // one lane per address: in order
+      }
       if ((pair + 1) % M == 0) {
         __syncthreads();  // every wave's rows of the group are in acc
         // The group's slots are written again one group later, after the next barrier,
         // which no thread passes before finishing this flush.
-        flush(pair + 1 - M, M, grp_c, grp_n);
+        if constexpr (!kCarry) flush(pair + 1 - M, M, grp_c, grp_n);
         grp_c = c_nx;
         grp_n = n_nx;
       }
@@ -591,6 +631,7 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     // Three phases, each storing its output before the next one's loads are issued (a
     // memory clobber between them keeps the compiler from hoisting every reload to the top,
     // which would hold them all live at once).
+    if constexpr (!kCarry) {
     {
       float uv[kT];
       load_steps<Elem, kVecRows, true>(u_buf, e0, t0, L, end, uv);
@@ -640,6 +681,17 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         s_dDb[wave][hf][1] += sb;
       }
     }
+    }
+  }
+  if constexpr (kCarry) {
+    // the segment's adjoint from a zero start, and its sum of step sizes
+    const float sp = half_sum_to_last(seg_sdt);
+    if (active) {
+      const int64_t r = int64_t(seg) * p.rows + row;
+      for (int n = li; n < N; n += kHalfLanes) p.cq[r * N + n] = s_adj[wave][hf][n];
+      if (half_end) p.cp[r] = sp;
+    }
+    return;
   }
   if (total % M != 0) {  // the last, partly filled group
     __syncthreads();
@@ -648,19 +700,22 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
 
   const float sD = s_dDb[wave][hf][0], sb = s_dDb[wave][hf][1];
   if (active) {
-    // s_adj and s_dA were last written by lanes of this wave; LDS keeps a wave's order
+    // s_adj and s_dA were last written by lanes of this wave; LDS keeps a wave's order. With
+    // segments, dh0 comes from the first one, and dA, dD and dbias go into this segment's
+    // slots (the reduction adds the segments too).
+    const int64_t srow = kSeg ? int64_t(seg) * p.rows + row : row;
     for (int n = li; n < N; n += kHalfLanes) {
       const float dAv = s_dA[wave][hf][n];
-      if (p.dh0) p.dh0[row * N + n] = s_adj[wave][hf][n];  // e_{-1} = a_0 g_0
+      if (p.dh0 && (!kSeg || seg == 0)) p.dh0[row * N + n] = s_adj[wave][hf][n];  // e_{-1} = a_0 g_0
       if (p.partials)
-        p.dA[row * N + n] = dAv;
+        p.dA[srow * N + n] = dAv;
       else
         unsafeAtomicAdd(&p.dA[int64_t(d) * N + n], dAv);
     }
     if (half_end) {
       if (p.partials) {
-        if (p.dD) p.dD[row] = sD;
-        if (p.dbias) p.dbias[row] = sb;
+        if (p.dD) p.dD[srow] = sD;
+        if (p.dbias) p.dbias[srow] = sb;
       } else {
         if (p.dD) unsafeAtomicAdd(&p.dD[d], sD);
         if (p.dbias) unsafeAtomicAdd(&p.dbias[d], sb);
@@ -669,9 +724,34 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   }
 }
 
+// Between the carry launch and the main one of a segmented backward: per (row, state), the
+// adjoint entering each segment from the right, from the last segment down. Segment s maps
+// the e entering it to the e leaving its first step, e -> exp(A sum s) e + q_s (q_s its
+// adjoint from a zero start, written by the carry launch); the last segment starts from
+// dfinal. Each q_s is read before its slot receives the e entering segment s, which is what
+// the main launch reads (slot 0, which no carry fills, receives segment 0's).
+__global__ __launch_bounds__(256) void bwd_carry_kernel(const float* A, const float* dfinal,
+                                                        float* cq, const float* cp, int64_t rows,
+                                                        int64_t dim, int dstate, int nseg) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= rows * dstate) return;
+  const int64_t row = i / dstate;
+  const int n = int(i - row * dstate);
+  const float a2 = A[(row % dim) * dstate + n] * kLog2e;
+  float e = dfinal ? dfinal[i] : 0.0f;
+  for (int s = nseg - 1; s >= 1; --s) {
+    const int64_t r = int64_t(s) * rows + row;
+    const float q = cq[r * dstate + n];
+    cq[r * dstate + n] = e;
+    e = __builtin_fmaf(exp2_hw(cp[r] * a2), e, q);
+  }
+  cq[row * dstate + n] = e;
+}
+
 // The second launch of a backward with a workspace: every summed gradient is the sum of its
 // partials in a fixed order (no atomics). grid.y = 0: dB and dC, element (b, n, t) summed
-// over the batch row's workgroups; grid.y = 1: dA, dD and dbias summed over batch rows.
+// over the batch row's workgroups; grid.y = 1: dA, dD and dbias summed over the segments'
+// batch rows.
 struct RParams {
   const float* part;
   const float* part_dA;
@@ -683,6 +763,7 @@ struct RParams {
   float* dD;      // nullable
   float* dbias;   // nullable
   int64_t batch, dim, dstate, seqlen, groups;
+  int64_t seg_rows;  // rows of dA, dD and dbias partials: segments x batch rows
 };
 
 // The workgroups g of a batch row are split into kSlices runs of consecutive g; eight
@@ -754,7 +835,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(RParams r) {
       }
       if (!dst) continue;
       float s = 0.0f;
-      for (int64_t b = 0; b < r.batch; ++b) s += src[b * gs + e];
+      for (int64_t b = 0; b < r.seg_rows; ++b) s += src[b * gs + e];
       dst[e] = s;
     }
   }
@@ -805,18 +886,70 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   p.n_ckpt = int((a.seqlen + kCkptInterval - 1) / kCkptInterval);
   BwdWorkspace ws{};
   p.partials = a.workspace ? 1 : 0;
+  const int64_t nseg = a.workspace ? a.segments : 1;
+  const int64_t n_chunks = bwd_intervals(a.seqlen);
+  p.nseg = int(nseg);
+  p.seg0 = 0;
+  p.seg_chunks = int((n_chunks + nseg - 1) / nseg);
+  p.wgs = int(a.batch * p.dblocks);
+  p.rows = a.batch * a.dim;
+  p.cq = nullptr;
+  p.cp = nullptr;
+  if (nseg < 1 || (nseg > 1 && (nseg - 1) * p.seg_chunks >= n_chunks))
+    return int(hipErrorInvalidValue);  // every segment holds at least one interval
   if (a.workspace) {
-    if (!bwd_workspace(a.batch, a.dim, a.dstate, a.seqlen, a.io, &ws) || ws.groups != p.dblocks)
+    if (!bwd_workspace(a.batch, a.dim, a.dstate, a.seqlen, a.io, nseg, &ws) ||
+        ws.groups != p.dblocks)
       return int(hipErrorInvalidValue);
     p.dB = a.workspace + ws.part;
     p.dC = nullptr;
     p.dA = a.workspace + ws.dA;
     p.dD = a.dD ? a.workspace + ws.dD : nullptr;
     p.dbias = a.dbias ? a.workspace + ws.dbias : nullptr;
+    if (nseg > 1) {
+      p.cq = a.workspace + ws.cq;
+      p.cp = a.workspace + ws.cp;
+    }
   }
-  const int64_t blocks = a.batch * p.dblocks;
+  const int64_t blocks = nseg * p.wgs;
   const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * W);
-  if (a.vec_ok) {
+  if (nseg > 1) {
+    // The carry launch: segments 1 .. nseg - 1 (segment 0's carry is never needed).
+    BParams pc = p;
+    pc.seg0 = 1;
+    const dim3 cgrid = dim3(unsigned((nseg - 1) * p.wgs));
+    if (a.vec_ok) {
+      if (a.mask)
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, true, true, true>), cgrid, block, 0, s, pc);
+      else
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, false, true, true>), cgrid, block, 0, s, pc);
+    } else {
+      if (a.mask)
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, true, true, true>), cgrid, block, 0, s, pc);
+      else
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, false, true, true>), cgrid, block, 0, s, pc);
+    }
+    int st = int(hipGetLastError());
+    if (st != 0) return st;
+    const int64_t items = p.rows * a.dstate;
+    hipLaunchKernelGGL(bwd_carry_kernel, dim3(unsigned((items + 255) / 256)), dim3(256), 0, s,
+                       a.A, a.dfinal, p.cq, p.cp, p.rows, a.dim, int(a.dstate), int(nseg));
+    st = int(hipGetLastError());
+    if (st != 0) return st;
+  }
+  if (nseg > 1) {
+    if (a.vec_ok) {
+      if (a.mask)
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, true, true>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, false, true>), grid, block, 0, s, p);
+    } else {
+      if (a.mask)
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, true, true>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, false, true>), grid, block, 0, s, p);
+    }
+  } else if (a.vec_ok) {
     if (a.mask)
       hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, true>), grid, block, 0, s, p);
     else
@@ -844,6 +977,7 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   r.dstate = a.dstate;
   r.seqlen = a.seqlen;
   r.groups = ws.groups;
+  r.seg_rows = nseg * a.batch;
   const bool v4 = (a.dstate * a.seqlen) % 4 == 0 && reinterpret_cast<uintptr_t>(a.dB) % 16 == 0 &&
                   reinterpret_cast<uintptr_t>(a.dC) % 16 == 0;
   const int64_t cols = a.batch * 2 * a.dstate * a.seqlen / (v4 ? 4 : 1);

@@ -619,21 +619,6 @@ __global__ __launch_bounds__(64) void debug_wave_combine_kernel(const float* a, 
   b_out[i] = bv;
 }
 
-// Compute units of the current device, read once per device.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 // Whether an fp32 launch splits each channel's states over two waves. One wave per channel
 // leaves most SIMDs with a single wave when there are few channels. A two-wave workgroup (K
@@ -737,6 +722,22 @@ int launch_typed(const FwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Compute units of the current device, read once per device (declared in scan_launch.h).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 // Launch shapes: steps per lane, channels per workgroup, states per LDS stage.
 #ifndef SSM_BF16_T

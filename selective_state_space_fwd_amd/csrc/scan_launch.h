@@ -71,11 +71,15 @@ struct BwdArgs {
   float* dh0;            // nullable
   const uint8_t* mask;   // nullable: [batch, seqlen], 0 = padding step
   float* workspace;      // nullable: per-workgroup partial sums (BwdWorkspace); NULL = atomics
+  int64_t segments;      // with a workspace laid out for that many segments; else 1
   int64_t batch, dim, dstate, seqlen;
   Io io;
   bool softplus;
   bool vec_ok;
 };
+
+// Compute units of the current device (read once per device; 0 if the runtime refuses).
+int device_cus();
 
 // Wavefronts per backward workgroup, by storage type (two channels per wavefront), and the
 // number of (interval, state) steps between its barriers. One 16-wave workgroup per CU
@@ -92,22 +96,50 @@ constexpr int kBwdGroup = SSM_BWD_GROUP;
 constexpr int kBwdChannelsBf16 = 2 * kBwdWavesBf16;
 constexpr int kBwdChannelsF32 = 2 * kBwdWavesF32;
 
-// The backward's workspace, in floats from its start, every region 256-byte aligned:
+// The backward's workspace, in floats from its start, every region 256-byte aligned, with S
+// segments (each channel's sequence cut into S runs of whole saved-state intervals, each run
+// its own workgroup; S = 1: no cut):
 //   part  [batch][groups][2][dstate][seqlen]  each workgroup's sums of dB (0) and dC (1)
 //                                             over its channels, groups = ceil(dim / K)
-//   dA    [batch][dim][dstate]                each batch row's dA
-//   dD    [batch][dim]                        each batch row's dD
-//   dbias [batch][dim]                        each batch row's dbias
+//                                             (the segments of a group fill disjoint steps)
+//   dA    [S][batch][dim][dstate]             each segment's and batch row's dA
+//   dD    [S][batch][dim]                     likewise dD
+//   dbias [S][batch][dim]                     likewise dbias
+//   cq    [S][batch][dim][dstate]             S > 1: each segment's state adjoint from a
+//                                             zero start at its right end (segment 0 unused)
+//   cp    [S][batch][dim]                     S > 1: each segment's sum of step sizes
 // A second launch sums these in a fixed order, so every gradient is reproducible.
 struct BwdWorkspace {
-  int64_t groups;
-  int64_t part, dA, dD, dbias;  // offsets in floats
-  int64_t floats;               // total size in floats
+  int64_t groups, segments;
+  int64_t part, dA, dD, dbias, cq, cp;  // offsets in floats
+  int64_t floats;                       // total size in floats
 };
+
+// Intervals of kCkptInterval steps in a sequence.
+inline int64_t bwd_intervals(int64_t seqlen) {
+  return seqlen / kCkptInterval + (seqlen % kCkptInterval != 0);
+}
+
+// The segments a backward with a workspace cuts each sequence into on a device with `cus`
+// compute units: none while the workgroups of whole sequences (one per batch row and group of
+// channels) fill the device, otherwise as many as fill it, at most one per interval, each of
+// ceil(intervals / S) intervals (so none is empty).
+inline int64_t bwd_segments(int64_t batch, int64_t dim, int64_t seqlen, Io io, int cus) {
+  const int64_t k = io == Io::BF16 ? kBwdChannelsBf16 : kBwdChannelsF32;
+  const int64_t groups = dim / k + (dim % k != 0);  // no overflow for any dim
+  // (past the device's size in either factor the workgroups fill it: no product formed)
+  if (cus <= 0 || batch <= 0 || groups <= 0 || batch >= cus || groups >= cus) return 1;
+  const int64_t wgs = batch * groups, n = seqlen / kCkptInterval + (seqlen % kCkptInterval != 0);
+  if (wgs >= cus || n < 2) return 1;
+  int64_t s = cus / wgs;
+  if (s > n) s = n;
+  const int64_t per = (n + s - 1) / s;
+  return (n + per - 1) / per;
+}
 
 // false on overflow of int64 sizes.
 inline bool bwd_workspace(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, Io io,
-                          BwdWorkspace* w) {
+                          int64_t segments, BwdWorkspace* w) {
   const int64_t k = io == Io::BF16 ? kBwdChannelsBf16 : kBwdChannelsF32;
   const int64_t lim = int64_t(1) << 60;
   auto mul = [&](int64_t x, int64_t y, int64_t* r) {
@@ -118,14 +150,19 @@ inline bool bwd_workspace(int64_t batch, int64_t dim, int64_t dstate, int64_t se
   auto round64 = [](int64_t x) { return (x + 63) / 64 * 64; };  // 256 bytes of floats
   int64_t part, rows, rn;
   w->groups = (dim + k - 1) / k;
+  w->segments = segments < 1 ? 1 : segments;
   if (!mul(batch, w->groups, &part) || !mul(part, 2 * dstate, &part) ||
-      !mul(part, seqlen, &part) || !mul(batch, dim, &rows) || !mul(rows, dstate, &rn))
+      !mul(part, seqlen, &part) || !mul(batch, dim, &rows) || !mul(rows, w->segments, &rows) ||
+      !mul(rows, dstate, &rn))
     return false;
+  const bool carry = w->segments > 1;
   w->part = 0;
   w->dA = round64(part);
   w->dD = w->dA + round64(rn);
   w->dbias = w->dD + round64(rows);
-  w->floats = w->dbias + round64(rows);
+  w->cq = w->dbias + round64(rows);
+  w->cp = w->cq + (carry ? round64(rn) : 0);
+  w->floats = w->cp + (carry ? round64(rows) : 0);
   return w->floats < lim;
 }
 

@@ -16,6 +16,8 @@
 namespace {
 int g_launches = 0;
 int64_t g_last_rows = -1;
+int64_t g_last_segments = -1;
+int g_cus = 0;  // compute units the stubbed device reports (0: no device)
 }  // namespace
 
 namespace ssm {
@@ -33,8 +35,10 @@ int launch_fill_zero(float*, int64_t, void*) {
 int launch_scan_bwd(const BwdArgs& a, void*) {
   ++g_launches;
   g_last_rows = a.batch * a.dim;
+  g_last_segments = a.segments;
   return 0;
 }
+int device_cus() { return g_cus; }
 int launch_ssd_fwd(const SsdArgs& a, void*) {
   ++g_launches;
   g_last_rows = a.batch * a.nheads * a.headdim;
@@ -134,6 +138,34 @@ void scan_backward_checks() {
   EXPECT(ws > 0 && ws % 256 == 0);
   EXPECT(ssm_scan_bwd_workspace_bytes(-1, 1, 1, 1, 0) == -1);
   EXPECT(ssm_scan_bwd_workspace_bytes(1, 1, 1, 1, 2) == -1);
+
+  // Segments, on a stubbed 256-CU device: few channels and a long sequence are cut (more
+  // workspace); the unsplit size still works, with one segment; the layer's shape is not cut.
+  g_cus = 256;
+  const uint32_t fl = SSM_IO_F32 | SSM_DELTA_SOFTPLUS;
+  const int64_t big = ssm_scan_bwd_workspace_bytes(2, 512, 16, 8192, fl);
+  const int64_t one = ssm_scan_bwd_workspace_bytes(2, 512, 16, 8192, fl | SSM_BWD_UNSPLIT);
+  EXPECT(big > one && one > 0);
+  auto bwd = [&](uint32_t flags, int64_t wsb, int64_t L) {
+    return ssm_scan_bwd(at(0), at(1), at<const float>(2), at(3), at(4), at<const float>(5),
+                        nullptr, at<const float>(7), nullptr, flags, at<const float>(10), at(11),
+                        at<const float>(12), at(13), at(14), at<float>(15), at<float>(16),
+                        at<float>(17), at<float>(18), nullptr, at<float>(20), at<float>(21),
+                        at(22), wsb, 2, 512, 16, L, nullptr);
+  };
+  EXPECT(bwd(fl, big, 8192) == SSM_OK && g_last_segments == 8);  // 32 groups x 8 = 256
+  EXPECT(bwd(fl, one, 8192) == SSM_OK && g_last_segments == 1);
+  EXPECT(bwd(fl | SSM_BWD_UNSPLIT, big, 8192) == SSM_OK && g_last_segments == 1);
+  EXPECT(bwd(fl, one - 256, 8192) == SSM_ERR_INVALID_ARG);
+  // 3 intervals: at most 3 segments, one interval each
+  const int64_t w3 = ssm_scan_bwd_workspace_bytes(2, 512, 16, 600, fl);
+  EXPECT(bwd(fl, w3, 600) == SSM_OK && g_last_segments == 3);
+  // 5 intervals on room for 4 segments: 2 intervals each, so 3 segments
+  g_cus = 4 * 32;
+  const int64_t w5 = ssm_scan_bwd_workspace_bytes(2, 512, 16, 5 * 256, fl);
+  EXPECT(bwd(fl, w5, 5 * 256) == SSM_OK && g_last_segments == 3);
+  EXPECT(ssm_scan_bwd_workspace_bytes(4, 2048, 16, 2048, SSM_IO_BF16) == ws);  // 256 groups
+  g_cus = 0;
 }
 
 int ssd(int64_t b, int64_t h, int64_t p, int64_t n, int64_t L, int64_t ws_bytes) {

@@ -47,7 +47,7 @@ def setup(w, softplus=True, use_D=True, use_z=True, use_bias=True, dfinal=True, 
     return inp, dout, dfin
 
 
-def run_gpu(inp, dout, dfin, softplus, deterministic=True, workspace=None):
+def run_gpu(inp, dout, dfin, softplus, deterministic=True, workspace=None, unsplit=False):
     io = inp["io"]
     g = {k: dev(inp[k], io) for k in ("u", "delta", "B", "C", "z")}
     f = {k: dev(inp[k], "f32") for k in ("A", "D", "delta_bias", "h0")}
@@ -58,7 +58,8 @@ def run_gpu(inp, dout, dfin, softplus, deterministic=True, workspace=None):
                               dev(dout, io), D=f["D"], z=g["z"], delta_bias=f["delta_bias"],
                               delta_softplus=softplus,
                               dfinal=None if dfin is None else dev(dfin, "f32"),
-                              deterministic=deterministic, workspace=workspace)
+                              deterministic=deterministic, workspace=workspace,
+                              unsplit=unsplit)
     torch().cuda.synchronize()
     res = {k: (None if v is None else host(v)) for k, v in grads.items()}
     return host(out), host(fin), host(states), res
@@ -210,7 +211,8 @@ def test_backward_atomic_path(shape, io):
 
 def test_backward_workspace_reused_and_paths_agree():
     """One caller-held workspace, larger than needed, serves two different problems in a
-    row; on the same problem the two summation paths agree within float32 rounding and the
+    row; on the same problem the two summation paths agree within float32 rounding and, with
+    the sequences kept whole (SSM_BWD_UNSPLIT, as the atomic path keeps them), the
     per-element gradients are identical."""
     t = torch()
     need = max(ssm.ssm_scan_bwd_workspace_bytes(2, 40, 16, 900, ssm.SSM_IO_BF16),
@@ -221,7 +223,7 @@ def test_backward_workspace_reused_and_paths_agree():
                                     initial_state=True, seed=67 + i)
         announce(w.describe() + " workspace reuse")
         inp, dout, dfin = setup(w, seed=67 + i)
-        *_, gw = run_gpu(inp, dout, dfin, True, workspace=ws)
+        *_, gw = run_gpu(inp, dout, dfin, True, workspace=ws, unsplit=True)
         compare("bf16", gw, run_oracle(inp, dout, dfin, True), w.describe() + " reused ws")
         *_, ga = run_gpu(inp, dout, dfin, True, deterministic=False)
         for k in ("du", "ddelta", "dz", "dh0"):
@@ -230,6 +232,43 @@ def test_backward_workspace_reused_and_paths_agree():
             rep = parity(ga[k], gw[k].astype(np.float64), 1e-5)
             print(f"[paths] {k}: {rep}", flush=True)
             assert rep.ok, f"{k}: {rep}"
+
+
+def _segments(b, d, L, io):
+    """The segments the library cuts each sequence into here: the workspace sizes with and
+    without SSM_BWD_UNSPLIT differ exactly when it cuts (the carries and per-segment slots)."""
+    flags = ssm.SSM_IO_BF16 if io == "bf16" else ssm.SSM_IO_F32
+    return (ssm.ssm_scan_bwd_workspace_bytes(b, d, 16, L, flags)
+            > ssm.ssm_scan_bwd_workspace_bytes(b, d, 16, L, flags | ssm.SSM_BWD_UNSPLIT))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(4, 320, 16, 2700), (1, 37, 16, 4100), (2, 40, 16, 600)],
+                         ids=lambda s: "b{}d{}N{}L{}".format(*s))
+def test_backward_segments(shape, io):
+    """Few channels, long sequences: the workspace path cuts each sequence into segments
+    (on a 256-CU device: 6 segments of two intervals, the last of one, for the first shape;
+    one interval each for the others), each scanned from the adjoint carried into it. Every
+    gradient against the oracle, bitwise reproducible, and within float32 rounding of the
+    uncut backward."""
+    b, d, n, L = shape
+    w = WORKLOADS["tiny"].with_(batch=b, dim=d, dstate=n, seqlen=L, io=io, gate=True,
+                                initial_state=True, seed=800 + L)
+    announce(w.describe() + " backward in segments")
+    assert _segments(b, d, L, io), "expected the sequence to be cut into segments"
+    inp, dout, dfin = setup(w, seed=L + 3)
+    *_, g1 = run_gpu(inp, dout, dfin, True)
+    compare(io, g1, run_oracle(inp, dout, dfin, True), w.describe() + " segments")
+    *_, g2 = run_gpu(inp, dout, dfin, True)
+    for k in ALL_GRADS:
+        assert np.array_equal(g1[k], g2[k]), k
+    *_, gu = run_gpu(inp, dout, dfin, True, unsplit=True)
+    for k in ALL_GRADS:
+        # bf16 per-element outputs: float32 values 1e-5 apart may round one bf16 step apart
+        tol = 2.0 ** -8 * 1.01 if (io == "bf16" and k in PER_ELEMENT) else 1e-5
+        rep = parity(g1[k].astype(np.float32), gu[k].astype(np.float64), tol)
+        print(f"[segments vs whole] {k}: {rep}", flush=True)
+        assert rep.ok, f"{k}: {rep}"
 
 
 def test_backward_layer_workload_full():
