@@ -66,11 +66,12 @@ struct BParams {
   int partials;
   // Segments: each channel's sequence cut into nseg runs of seg_chunks intervals (the last
   // maybe shorter), each its own workgroup; workgroup blockIdx.x takes segment
-  // seg0 + blockIdx.x / wgs of group blockIdx.x % wgs (wgs = batch dblocks). rows = batch
-  // dim: the stride of one segment's slots of dA, dD, dbias and the carries. cq, cp: each
-  // segment's state adjoint from a zero start at its right end, [nseg][rows][dstate], and its
-  // sum of step sizes, [nseg][rows] (written by the carry launch, read by the main one).
-  int nseg, seg0, seg_chunks, wgs;
+  // blockIdx.x / wgs of group blockIdx.x % wgs (wgs = batch dblocks). rows = batch dim: the
+  // stride of one segment's slots of dA, dD, dbias and the carries. cq, cp: each segment's
+  // state adjoint from a zero start at its right end, [nseg][rows][dstate], and its sum of
+  // step sizes, [nseg][rows] (written by the carry launch; bwd_carry_kernel then turns cq
+  // into the adjoint entering each segment, which the main launch reads).
+  int nseg, seg_chunks, wgs;
   int64_t rows;
   float* cq;
   float* cp;
@@ -247,13 +248,10 @@ __device__ __forceinline__ void store_steps(const Buf& b, uint32_t e0, int t0, i
 // rows of dB and dC have 2 M slots, so that one group of M states is written while the
 // previous one is added up. kMask: read a padding mask (its own instantiation: the unmasked
 // kernel's register count decides how many waves fit on a SIMD). kSeg: a segmented backward
-// (the workgroup takes one segment of its channels' sequences; its own instantiation, so that
-// the whole-sequence kernel's code is not touched). kCarry: the carry launch of a segmented
-// backward: only the state adjoint of each segment from a zero start at its right end (the
-// step sizes, a_t and c_t = C_t dy_t; no recomputed state, no gradient), stored with the
-// segment's sum of step sizes.
-template <typename Elem, int W, int M, bool kVecRows, bool kMask, bool kSeg = false,
-          bool kCarry = false>
+// (the workgroup takes one segment of its channels' sequences, starting from the adjoint
+// carried into it; its own instantiation, so that the whole-sequence kernel's code is not
+// touched).
+template <typename Elem, int W, int M, bool kVecRows, bool kMask, bool kSeg = false>
 __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   constexpr int kVec = Vec<Elem>::kN;
   constexpr int kSteps = kCkptInterval;  // steps per interval
@@ -279,9 +277,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const int hf = lane >> 5;         // which of the wave's two channels
   const int li = lane & 31;         // lane inside the channel
   const bool half_start = li == 0, half_end = li == kHalfLanes - 1;
-  static_assert(kSeg || !kCarry, "the carry launch belongs to a segmented backward");
-  const int seg = kSeg ? p.seg0 + int(blockIdx.x) / p.wgs : 0;
-  const int wg = kSeg ? int(blockIdx.x) - (seg - p.seg0) * p.wgs : int(blockIdx.x);  // channels
+  const int seg = kSeg ? int(blockIdx.x) / p.wgs : 0;
+  const int wg = kSeg ? int(blockIdx.x) - seg * p.wgs : int(blockIdx.x);  // the channel group
   const int b = wg / p.dblocks;
   const int d0 = (wg - b * p.dblocks) * (2 * W) + 2 * wave;  // the wave's first channel
   // Uniform, but the compiler computes the clamp with a vector min/max (v_med3): taken back
@@ -320,9 +317,9 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
   const float bias_d = (active && p.bias) ? p.bias[d] : 0.0f;
   for (int n = li; n < N; n += kHalfLanes) {
     // e entering from the right: dfinal at the sequence's end (e_L); with segments, what
-    // bwd_carry_kernel combined for this segment. The carry launch starts from zero.
+    // bwd_carry_kernel combined for this segment.
     float e = 0.0f;
-    if (!kCarry && active) {
+    if (active) {
       if (kSeg)
         e = p.cq[(int64_t(seg) * p.rows + row) * N + n];
       else
@@ -440,7 +437,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
 
   int pair = 0;
   int grp_c = c_hi, grp_n = 0;  // the current group's first pair
-  float seg_sdt = 0.0f;         // the carry launch: this lane's sum of step sizes
   for (int c = c_hi; c >= c_lo; --c) {
     const int t0 = c * kSteps + li * kT;
     const uint32_t e0 = row_e + uint32_t(t0);
@@ -505,9 +501,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       }
       // Formed here: left to the compiler, the sum sinks to its use after the state loop
       // and keeps u live (and spilled) across it.
-      if constexpr (!kCarry) asm volatile("" : "+v"(dD_acc));
+      asm volatile("" : "+v"(dD_acc));
     }
-    if constexpr (kCarry) seg_sdt += sdt;
 
     for (int n = 0; n < N; ++n, ++pair) {
       const float An = A_nx, hc = hc_nx;
@@ -524,24 +519,21 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         const int grp = pair / M;
         if (pair % M == 0) stage_load(grp + 1, st_word);
         const float4* sB = &s_bc[grp & 1][pair % M][0][kT / 4 * li];
-        if constexpr (!kCarry) {
 #pragma unroll
-          for (int q = 0; q < kT / 4; ++q) {
-            const float4 bq = sB[q];
-            Bv[4 * q] = bq.x;
-            Bv[4 * q + 1] = bq.y;
-            Bv[4 * q + 2] = bq.z;
-            Bv[4 * q + 3] = bq.w;
-          }
+        for (int q = 0; q < kT / 4; ++q) {
+          const float4 bq = sB[q];
+          Bv[4 * q] = bq.x;
+          Bv[4 * q + 1] = bq.y;
+          Bv[4 * q + 2] = bq.z;
+          Bv[4 * q + 3] = bq.w;
         }
       }
-      // forward again from the saved state: h_t for this lane's steps (the carry launch
-      // needs only the a_t)
+      // forward again from the saved state: h_t for this lane's steps
       float bseg = half_start ? hc : 0.0f;
 #pragma unroll
       for (int j = 0; j < kT; ++j) {
         dA[j] = exp2_hw(sv[j] * a2);
-        if constexpr (!kCarry) bseg = __builtin_fmaf(dA[j], bseg, su[j] * Bv[j]);
+        bseg = __builtin_fmaf(dA[j], bseg, su[j] * Bv[j]);
       }
       const float alpha = exp2_hw(sdt * a2);  // product of the lane's a_t
       {
@@ -558,13 +550,13 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
           Cv[4 * q + 3] = cq.w;
         }
       }
-      if constexpr (!kCarry) {
+      {
         float aseg = alpha;
         half_scan_inclusive(aseg, bseg);  // bseg: the state after the lane's last step
       }
-      const float up = kCarry ? 0.0f : shift_up_any(bseg);
+      const float up = shift_up_any(bseg);
       const float hin = half_start ? hc : up;  // the state entering the lane's steps
-      if constexpr (!kCarry) {
+      {
         float hh = hin;
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
@@ -589,7 +581,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
                                                                        // to the left
       // dB and dC rows of the step pairs (j, j + 4) are added across the two halves as
       // soon as both exist and go to LDS at once: four steps per lane, 8 li + 4 hf on.
-      if constexpr (!kCarry) {
       float dBr[kT / 2], dCr[kT / 2];
       const int slot = pair % kSlots;
       float* const rowB = reinterpret_cast<float*>(&acc[slot][0][wave][2 * li + hf]);
@@ -616,12 +607,11 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
       }
       dAn = half_sum_to_last(dAn);
       if (half_end) atomicAdd(&s_dA[wave][hf][n], dAn);  // one lane per address: in order
-      }
       if ((pair + 1) % M == 0) {
         __syncthreads();  // every wave's rows of the group are in acc
         // The group's slots are written again one group later, after the next barrier,
         // which no thread passes before finishing this flush.
-        if constexpr (!kCarry) flush(pair + 1 - M, M, grp_c, grp_n);
+        flush(pair + 1 - M, M, grp_c, grp_n);
         grp_c = c_nx;
         grp_n = n_nx;
       }
@@ -631,7 +621,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     // Three phases, each storing its output before the next one's loads are issued (a
     // memory clobber between them keeps the compiler from hoisting every reload to the top,
     // which would hold them all live at once).
-    if constexpr (!kCarry) {
     {
       float uv[kT];
       load_steps<Elem, kVecRows, true>(u_buf, e0, t0, L, end, uv);
@@ -681,17 +670,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         s_dDb[wave][hf][1] += sb;
       }
     }
-    }
-  }
-  if constexpr (kCarry) {
-    // the segment's adjoint from a zero start, and its sum of step sizes
-    const float sp = half_sum_to_last(seg_sdt);
-    if (active) {
-      const int64_t r = int64_t(seg) * p.rows + row;
-      for (int n = li; n < N; n += kHalfLanes) p.cq[r * N + n] = s_adj[wave][hf][n];
-      if (half_end) p.cp[r] = sp;
-    }
-    return;
   }
   if (total % M != 0) {  // the last, partly filled group
     __syncthreads();
@@ -706,7 +684,8 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
     const int64_t srow = kSeg ? int64_t(seg) * p.rows + row : row;
     for (int n = li; n < N; n += kHalfLanes) {
       const float dAv = s_dA[wave][hf][n];
-      if (p.dh0 && (!kSeg || seg == 0)) p.dh0[row * N + n] = s_adj[wave][hf][n];  // e_{-1} = a_0 g_0
+      if (p.dh0 && (!kSeg || seg == 0))
+        p.dh0[row * N + n] = s_adj[wave][hf][n];  // e_{-1} = a_0 g_0
       if (p.partials)
         p.dA[srow * N + n] = dAv;
       else
@@ -721,6 +700,110 @@ __global__ __launch_bounds__(64 * W, 4) void scan_bwd_kernel(BParams p) {
         if (p.dbias) unsafeAtomicAdd(&p.dbias[d], sb);
       }
     }
+  }
+}
+
+// The carry launch of a segmented backward, for segments 1 .. nseg - 1: per (row, state), the
+// state adjoint leaving the segment's first step when zero enters it from the right, and per
+// row the segment's sum of step sizes. Only the adjoint's part of the backward: per interval
+// (last to first) the step sizes and dL/dy of the lane's 8 steps, then per state a_t, the
+// lane's fold from the right, the half's scan from the right and the carry across
+// intervals. The lanes are mapped as in scan_bwd_kernel (a wave owns two channels, lane i of
+// a half 8 consecutive steps of an interval); each wave is independent of the others: C is
+// read straight from memory (a half's 32 lanes read 256 consecutive steps of a row), and
+// nothing is staged or waited for across waves.
+constexpr int kCarryWaves = 4;
+
+template <typename Elem, bool kVecRows, bool kMask>
+__global__ __launch_bounds__(64 * kCarryWaves) void bwd_carry_scan_kernel(BParams p) {
+  __shared__ float s_e[kCarryWaves][2][kMaxStates];   // the adjoint carried across intervals
+  __shared__ float s_a2[kCarryWaves][2][kMaxStates];  // A log2(e) of the half's channel
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, li = lane & 31;
+  const bool half_start = li == 0, half_end = li == kHalfLanes - 1;
+  const int dblocks = (p.dim + 2 * kCarryWaves - 1) / (2 * kCarryWaves);
+  const int wgs = int(p.rows / p.dim) * dblocks;  // workgroups per segment
+  const int seg = 1 + int(blockIdx.x) / wgs;
+  const int wg = int(blockIdx.x) - (seg - 1) * wgs;
+  const int b = wg / dblocks;
+  const int d0 = (wg - b * dblocks) * (2 * kCarryWaves) + 2 * wave;
+  const int rows_here = __builtin_amdgcn_readfirstlane(
+      p.dim - d0 >= 2 ? 2 : (p.dim - d0 > 0 ? p.dim - d0 : 0));
+  const int d = d0 + hf;
+  const bool active = hf < rows_here;
+  const int N = p.dstate, L = p.seqlen;
+  constexpr int kSteps = kCkptInterval;
+  const int n_chunks = (L + kSteps - 1) / kSteps;
+  const int c_lo = seg * p.seg_chunks;
+  const int c_hi = (c_lo + p.seg_chunks < n_chunks ? c_lo + p.seg_chunks : n_chunks) - 1;
+  const int64_t row0 = int64_t(b) * p.dim + (rows_here > 0 ? d0 : 0);
+  const int64_t row = row0 + hf;
+  const uint32_t end = uint32_t(rows_here) * uint32_t(L);  // elements of the wave's rows
+  const uint32_t bytes = end * uint32_t(sizeof(Elem));
+  const Buf dl_buf(static_cast<const Elem*>(p.delta) + row0 * L, bytes);
+  const Buf do_buf(static_cast<const Elem*>(p.dout) + row0 * L, bytes);
+  const Buf z_buf(static_cast<const Elem*>(p.z ? p.z : p.delta) + row0 * L, p.z ? bytes : 0u);
+  const uint32_t bc_elems = uint32_t(N) * uint32_t(L);
+  const Buf C_buf(static_cast<const Elem*>(p.C) + int64_t(b) * N * L, bc_elems * sizeof(Elem));
+  const uint32_t row_e = uint32_t(hf) * uint32_t(L);
+  const Buf mask_buf(kMask ? p.mask + int64_t(b) * L : nullptr, kMask ? uint32_t(L) : 0u);
+  const float bias_d = (active && p.bias) ? p.bias[d] : 0.0f;
+  for (int n = li; n < N; n += kHalfLanes) {
+    s_e[wave][hf][n] = 0.0f;
+    s_a2[wave][hf][n] = active ? p.A[int64_t(d) * N + n] * kLog2e : 0.0f;
+  }
+  float seg_sdt = 0.0f;
+  for (int c = c_hi; c >= c_lo; --c) {
+    const int t0 = c * kSteps + li * kT;
+    const uint32_t e0 = row_e + uint32_t(t0);
+    float sv[kT], dyv[kT], sdt = 0.0f;
+    {
+      float xv[kT], dov[kT], zv[kT];
+      load_steps<Elem, kVecRows>(dl_buf, e0, t0, L, end, xv);
+      load_steps<Elem, kVecRows>(do_buf, e0, t0, L, end, dov);
+      load_steps<Elem, kVecRows>(z_buf, e0, t0, L, end, zv);
+      if (p.softplus) {
+#pragma unroll
+        for (int j = 0; j < kT; ++j) sv[j] = softplus_f(xv[j] + bias_d);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kT; ++j) sv[j] = xv[j] + bias_d;
+      }
+#pragma unroll
+      for (int j = 0; j < kT; ++j) {
+        float sj = sv[j];
+        if (t0 + j >= L || !active) sj = dov[j] = zv[j] = 0.0f;  // identity steps
+        if constexpr (kMask) {
+          const uint32_t m = t0 + j < L ? mask_buf.load1(uint32_t(t0 + j)) : 1u;
+          if (m == 0) sj = 0.0f;  // padding: the state is kept, the output still emitted
+        }
+        sv[j] = sj;
+        sdt += sj;
+        dyv[j] = p.z ? dov[j] * zv[j] * sigmoid_f(zv[j]) : dov[j];
+      }
+    }
+    seg_sdt += sdt;
+    for (int n = 0; n < N; ++n) {
+      float Cv[kT];
+      load_steps<Elem, kVecRows>(C_buf, uint32_t(n) * uint32_t(L) + uint32_t(t0), t0, L,
+                                 bc_elems, Cv);
+      const float a2 = s_a2[wave][hf][n];
+      float beta = 0.0f;
+#pragma unroll
+      for (int j = kT - 1; j >= 0; --j)
+        beta = exp2_hw(sv[j] * a2) * __builtin_fmaf(Cv[j], dyv[j], beta);
+      float ra = exp2_hw(sdt * a2), rb = beta;
+      half_scan_from_right(ra, rb);
+      const float G = s_e[wave][hf][n];
+      if (half_start) s_e[wave][hf][n] = __builtin_fmaf(ra, G, rb);
+    }
+  }
+  const float sp = half_sum_to_last(seg_sdt);
+  if (active) {
+    const int64_t r = int64_t(seg) * p.rows + row;
+    for (int n = li; n < N; n += kHalfLanes) p.cq[r * N + n] = s_e[wave][hf][n];
+    if (half_end) p.cp[r] = sp;
   }
 }
 
@@ -889,7 +972,6 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   const int64_t nseg = a.workspace ? a.segments : 1;
   const int64_t n_chunks = bwd_intervals(a.seqlen);
   p.nseg = int(nseg);
-  p.seg0 = 0;
   p.seg_chunks = int((n_chunks + nseg - 1) / nseg);
   p.wgs = int(a.batch * p.dblocks);
   p.rows = a.batch * a.dim;
@@ -914,20 +996,20 @@ int launch_bwd_typed(const BwdArgs& a, hipStream_t s) {
   const int64_t blocks = nseg * p.wgs;
   const dim3 grid = dim3(unsigned(blocks)), block = dim3(64 * W);
   if (nseg > 1) {
-    // The carry launch: segments 1 .. nseg - 1 (segment 0's carry is never needed).
-    BParams pc = p;
-    pc.seg0 = 1;
-    const dim3 cgrid = dim3(unsigned((nseg - 1) * p.wgs));
+    // The carry launch: segments 1 .. nseg - 1 (segment 0's carry is never needed), one
+    // workgroup per batch row, segment and 2 kCarryWaves channels.
+    const int64_t cwgs = a.batch * ((a.dim + 2 * kCarryWaves - 1) / (2 * kCarryWaves));
+    const dim3 cgrid = dim3(unsigned((nseg - 1) * cwgs)), cblock = dim3(64 * kCarryWaves);
     if (a.vec_ok) {
       if (a.mask)
-        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, true, true, true>), cgrid, block, 0, s, pc);
+        hipLaunchKernelGGL((bwd_carry_scan_kernel<Elem, true, true>), cgrid, cblock, 0, s, p);
       else
-        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, true, false, true, true>), cgrid, block, 0, s, pc);
+        hipLaunchKernelGGL((bwd_carry_scan_kernel<Elem, true, false>), cgrid, cblock, 0, s, p);
     } else {
       if (a.mask)
-        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, true, true, true>), cgrid, block, 0, s, pc);
+        hipLaunchKernelGGL((bwd_carry_scan_kernel<Elem, false, true>), cgrid, cblock, 0, s, p);
       else
-        hipLaunchKernelGGL((scan_bwd_kernel<Elem, W, M, false, false, true, true>), cgrid, block, 0, s, pc);
+        hipLaunchKernelGGL((bwd_carry_scan_kernel<Elem, false, false>), cgrid, cblock, 0, s, p);
     }
     int st = int(hipGetLastError());
     if (st != 0) return st;
